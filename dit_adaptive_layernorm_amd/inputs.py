@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs for the adaptive-LayerNorm producers.
+
+This module only draws random numbers and lays them out; it holds none of the
+producers' arithmetic.  It serves the parity tests (both the HIP path and the
+CPU oracle get the same arrays) and the benchmark.
+
+Recipe: numpy PCG64 seeded with SeedSequence([seed, stream_id]), one stream id
+per tensor; standard normal draws in float64, scaled by sigma, rounded to
+float32; bf16 tensors are then rounded to bf16 by torch's CPU conversion
+(round to nearest even).  bf16 tensors are returned as uint16 bit patterns.
+
+The workloads follow the shapes the pages measure (Wan-video 2520 x 3072 and
+4096 x 3072 rows, the decode-action 16 x 2048 row block, the six-way
+modulation producer at B1 S5070 D3072) with value distributions chosen per
+workload: activations N(0, 1), modulation operands N(0, 0.1), timestep
+embedding chunks N(0, 0.5), and for the FP4 producer a 1% Bernoulli mask of
+x20 outliers applied before the bf16 rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# One stream id per tensor role, so that adding a tensor never shifts another.
+STREAM = {"x": 1, "scale": 2, "shift": 3, "temb": 4, "table": 5, "params": 6,
+          "mod": 7, "outlier": 8}
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
+
+
+def to_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 with torch (library RTNE); uint16 bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def normal_f32(shape, sigma: float, seed: int, stream: int) -> np.ndarray:
+    return (rng(seed, stream).standard_normal(shape) * sigma).astype(np.float32)
+
+
+def normal_bf16(shape, sigma: float, seed: int, stream: int) -> np.ndarray:
+    return to_bf16_bits(normal_f32(shape, sigma, seed, stream))
+
+
+def outlier_bf16(shape, seed: int, stream: int, outlier_stream: int,
+                 p: float = 0.01, factor: float = 20.0) -> np.ndarray:
+    """N(0,1) with each element independently (probability p) scaled by factor."""
+    f = normal_f32(shape, 1.0, seed, stream)
+    mask = rng(seed, outlier_stream).random(shape) < p
+    f = np.where(mask, f * np.float32(factor), f).astype(np.float32)
+    return to_bf16_bits(f)
+
+
+# ---- the five workloads ----------------------------------------------------
+
+ACT_SCALE = 0.025
+EPS = 1e-5
+
+WORKLOADS = {
+    "bcast_fp8_16x2048": dict(kind="bcast", rows=16, dim=2048),
+    "ptok_fp8_2520x3072": dict(kind="ptok", rows=2520, dim=3072),
+    "table_fp8_2520x3072": dict(kind="table", rows=2520, dim=3072, chunks=6,
+                                shift_idx=0, scale_idx=1),
+    "modulation6_1x5070x3072": dict(kind="mod6", batch=1, seq=5070, dim=3072),
+    "ln_fp4_4096x3072": dict(kind="fp4", rows=4096, dim=3072),
+}
+
+
+def make(kind: str, seed: int = 0, rows: int = 0, dim: int = 0, chunks: int = 6,
+         shift_idx: int = 0, scale_idx: int = 1, batch: int = 1, seq: int = 0,
+         outliers: bool = True) -> dict:
+    """Inputs for one producer at any shape, same distributions as above.
+
+    kind: "ln" | "bcast" | "ptok" | "table" | "fp4" | "mod6".
+    """
+    s = STREAM
+    if kind == "mod6":
+        return dict(params=normal_f32((batch, seq, 6, dim), 1.0, seed, s["params"]),
+                    mod=normal_f32((6, dim), 0.1, seed, s["mod"]))
+    if kind == "fp4":
+        x = (outlier_bf16((rows, dim), seed, s["x"], s["outlier"]) if outliers
+             else normal_bf16((rows, dim), 1.0, seed, s["x"]))
+        return dict(x=x, eps=EPS)
+    d = dict(x=normal_bf16((rows, dim), 1.0, seed, s["x"]), act_scale=ACT_SCALE, eps=EPS)
+    if kind == "bcast":
+        d["scale"] = normal_bf16((dim,), 0.1, seed, s["scale"])
+        d["shift"] = normal_bf16((dim,), 0.1, seed, s["shift"])
+    elif kind == "ptok":
+        d["scale"] = normal_bf16((rows, dim), 0.1, seed, s["scale"])
+        d["shift"] = normal_bf16((rows, dim), 0.1, seed, s["shift"])
+    elif kind == "table":
+        d["temb"] = normal_bf16((rows, chunks, dim), 0.5, seed, s["temb"])
+        d["table"] = normal_f32((chunks, dim), 0.1, seed, s["table"])
+        d["shift_idx"] = shift_idx
+        d["scale_idx"] = scale_idx
+    elif kind != "ln":
+        raise ValueError(kind)
+    return d
+
+
+def workload(name: str, seed: int = 0) -> dict:
+    w = dict(WORKLOADS[name])
+    kind = w.pop("kind")
+    d = make(kind, seed=seed, **w)
+    d["kind"] = kind
+    return d

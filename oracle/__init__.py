@@ -1,0 +1,308 @@
+"""numpy front end of the plain C oracle (oracle/alnp_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg; the product package never imports it and shares
+no code with it.
+
+Arrays are numpy: bf16 as uint16 bit patterns, e4m3 / packed e2m1 as uint8,
+fp32 as float32.  Large row loops can be split over threads (`threads=`); the
+C calls release the GIL, each thread owns a disjoint block of rows, and the
+per-row arithmetic is unchanged, so the result does not depend on `threads`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+
+_SIGS = {
+    "orc_bf16_to_f32_n": [_P, _I64, _P],
+    "orc_f32_to_bf16_n": [_P, _I64, _P],
+    "orc_e4m3_decode_n": [_P, _I64, _P],
+    "orc_e4m3_encode_sat_n": [_P, _I64, _P],
+    "orc_e2m1_decode_n": [_P, _I64, _P],
+    "orc_e2m1_encode_n": [_P, _I64, _P],
+    "orc_ln_stats": [_P, _I64, _I64, _F, _P, _P],
+    "orc_ln_fp8": [_P, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_adaln_fp8_bcast": [_P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_adaln_fp8_ptok": [_P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_adaln_fp8_table": [_P, _P, _P, _I64, _I64, _I64, _F, _F, _I64, _I64,
+                            _P, _P, _P, _P],
+    "orc_adaln_fp8_f32ops": [_P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_fp4_block_quant_n": [_P, _I64, _P, _P],
+    "orc_fp4_pack": [_P, _I64, _P],
+    "orc_ln_fp4": [_P, _F, _I64, _I64, _P, _P, _P, _P, _P],
+    "orc_modulation6": [_P, _P, _I64, _I64, _P],
+}
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so (build it first with oracle/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build  # noqa: WPS433
+            _build.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def _row_blocks(rows, threads):
+    threads = max(1, min(int(threads), rows)) if rows else 1
+    step = -(-rows // threads) if rows else 0
+    return [(r0, min(rows, r0 + step)) for r0 in range(0, rows, step)] if rows else []
+
+
+def _parallel(rows, threads, fn):
+    blocks = _row_blocks(rows, threads)
+    if len(blocks) <= 1:
+        for r0, r1 in blocks:
+            fn(r0, r1)
+        return
+    with ThreadPoolExecutor(len(blocks)) as ex:
+        list(ex.map(lambda b: fn(*b), blocks))
+
+
+# ---- number formats -------------------------------------------------------
+
+def bf16_to_f32(b):
+    b = _c(b, np.uint16)
+    out = np.empty(b.shape, np.float32)
+    lib().orc_bf16_to_f32_n(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def f32_to_bf16(f):
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().orc_f32_to_bf16_n(_ptr(f), f.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(codes):
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e4m3_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_sat(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_encode_sat_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e2m1_decode(codes):
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e2m1_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e2m1_encode_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+# ---- row statistics -------------------------------------------------------
+
+def ln_stats(x, eps=1e-5):
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    lib().orc_ln_stats(_ptr(x), rows, dim, eps, _ptr(mean), _ptr(rstd))
+    return mean, rstd
+
+
+# ---- FP8 producers --------------------------------------------------------
+
+def _fp8_outputs(rows, dim, want_y):
+    out = np.empty((rows, dim), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    y = np.empty((rows, dim), np.float32) if want_y else None
+    return out, mean, rstd, y
+
+
+def _rowptr(a, r0, row_elems):
+    return None if a is None else a.ctypes.data + r0 * row_elems * a.itemsize
+
+
+def ln_fp8(x, act_scale, eps=1e-5, want_y=False, threads=1):
+    """LayerNorm (no affine) -> static-scale e4m3; returns (out, mean, rstd, y)."""
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_ln_fp8(_rowptr(x, r0, dim), act_scale, eps, r1 - r0, dim,
+                         _rowptr(out, r0, dim), _rowptr(mean, r0, 1),
+                         _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
+def adaln_fp8_bcast(x, scale, shift, act_scale, eps=1e-5, want_y=False, threads=1):
+    x = _c(x, np.uint16)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    rows, dim = x.shape
+    assert scale.shape == (dim,) and shift.shape == (dim,)
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_adaln_fp8_bcast(_rowptr(x, r0, dim), _ptr(scale), _ptr(shift),
+                                  act_scale, eps, r1 - r0, dim,
+                                  _rowptr(out, r0, dim), _rowptr(mean, r0, 1),
+                                  _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
+def adaln_fp8_ptok(x, scale, shift, act_scale, eps=1e-5, want_y=False, threads=1):
+    x = _c(x, np.uint16)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    rows, dim = x.shape
+    assert scale.shape == (rows, dim) and shift.shape == (rows, dim)
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_adaln_fp8_ptok(_rowptr(x, r0, dim), _rowptr(scale, r0, dim),
+                                 _rowptr(shift, r0, dim), act_scale, eps,
+                                 r1 - r0, dim, _rowptr(out, r0, dim),
+                                 _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1),
+                                 _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
+def adaln_fp8_table(x, temb, table, shift_idx, scale_idx, act_scale, eps=1e-5,
+                    want_y=False, threads=1):
+    x = _c(x, np.uint16)
+    temb = _c(temb, np.uint16)
+    table = _c(table, np.float32)
+    rows, dim = x.shape
+    chunks = temb.shape[1]
+    assert temb.shape == (rows, chunks, dim) and table.shape == (chunks, dim)
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_adaln_fp8_table(_rowptr(x, r0, dim), _rowptr(temb, r0, chunks * dim),
+                                  _ptr(table), chunks, shift_idx, scale_idx,
+                                  act_scale, eps, r1 - r0, dim,
+                                  _rowptr(out, r0, dim), _rowptr(mean, r0, 1),
+                                  _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
+def adaln_fp8_f32ops(x, scale_f32, shift_f32, act_scale, eps=1e-5, want_y=False):
+    """Per-token core fed fp32 operands (rows, dim) directly."""
+    x = _c(x, np.uint16)
+    sc = _c(scale_f32, np.float32)
+    sh = _c(shift_f32, np.float32)
+    rows, dim = x.shape
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+    lib().orc_adaln_fp8_f32ops(_ptr(x), _ptr(sc), _ptr(sh), act_scale, eps, rows,
+                               dim, _ptr(out), _ptr(mean), _ptr(rstd), _ptr(y))
+    return out, mean, rstd, y
+
+
+# ---- FP4 producer ---------------------------------------------------------
+
+def fp4_block_quant(b):
+    """b: (..., 16k) fp32 -> (codes uint8 per element, scale codes per block)."""
+    b = _c(b, np.float32)
+    assert b.size % 16 == 0
+    codes = np.empty(b.shape, np.uint8)
+    scales = np.empty(b.shape[:-1] + (b.shape[-1] // 16,), np.uint8)
+    lib().orc_fp4_block_quant_n(_ptr(b), b.size // 16, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def fp4_pack(codes):
+    c = _c(codes, np.uint8)
+    assert c.shape[-1] % 2 == 0
+    out = np.empty(c.shape[:-1] + (c.shape[-1] // 2,), np.uint8)
+    lib().orc_fp4_pack(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def ln_fp4(x, eps=1e-5, want_b=False, threads=1):
+    """LayerNorm (no affine) -> bf16 stage -> e2m1 packed + e4m3 block scales.
+
+    Returns (packed (rows, dim/2), sf (rows, dim/16), mean, rstd, b)."""
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    assert dim % 16 == 0
+    packed = np.empty((rows, dim // 2), np.uint8)
+    sf = np.empty((rows, dim // 16), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    b = np.empty((rows, dim), np.float32) if want_b else None
+
+    def run(r0, r1):
+        lib().orc_ln_fp4(_rowptr(x, r0, dim), eps, r1 - r0, dim,
+                         _rowptr(packed, r0, dim // 2), _rowptr(sf, r0, dim // 16),
+                         _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1),
+                         _rowptr(b, r0, dim))
+    _parallel(rows, threads, run)
+    return packed, sf, mean, rstd, b
+
+
+# ---- six-way modulation ---------------------------------------------------
+
+def modulation6(params, mod, threads=1):
+    """params (B, S, 6, D) fp32 + mod (6, D) fp32 -> (6, B, S, D) bf16 bits."""
+    params = _c(params, np.float32)
+    mod = _c(mod, np.float32)
+    B, S, six, D = params.shape
+    assert six == 6 and mod.shape == (6, D)
+    tokens = B * S
+    out = np.empty((6, tokens, D), np.uint16)
+    if threads <= 1 or tokens < 2:
+        lib().orc_modulation6(_ptr(params), _ptr(mod), tokens, D, _ptr(out))
+    else:
+        # Each block of tokens writes its own token range of every plane.
+        parts = {}
+
+        def run(t0, t1):
+            o = np.empty((6, t1 - t0, D), np.uint16)
+            lib().orc_modulation6(_rowptr(params, t0, 6 * D), _ptr(mod), t1 - t0,
+                                  D, _ptr(o))
+            parts[t0] = (t1, o)
+        _parallel(tokens, threads, run)
+        for t0, (t1, o) in parts.items():
+            out[:, t0:t1] = o
+    return out.reshape(6, B, S, D)

@@ -1,0 +1,103 @@
+/*
+ * alnp_oracle.h -- plain, slow CPU oracle for the adaptive-LayerNorm producers.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may include, link or call this code; only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * source with the HIP path.
+ *
+ * Every function is the step-by-step definition of what the producers compute,
+ * written with scalar loops, separately rounded fp32 operations (compiled with
+ * -ffp-contract=off, no fast-math) and double-accumulated row statistics.
+ * Conversions to bf16 / e4m3 / e2m1 are done by nearest-value search over the
+ * format's finite values, not by bit tricks, so that a reader can check them
+ * against the format definitions by eye.
+ *
+ * Sources (web pages; cited by title and section):
+ *  - "adaptive-layernorm-producers" README, sections "Available Functions",
+ *    "Tensor Contract", "Minimal Usage", "Validation".
+ *  - "adaptive-layernorm-producers Benchmark Results", section
+ *    "Six-way modulation producer".
+ *  - h3-blackwell-runtime compare page: "NVFP4 Modulation Producer Fusion",
+ *    subsection "Exactness Contract" (operation order (x*(scale+1))+shift);
+ *    benchmarks/gb10-cute-p1-stream-a-summary.json, object
+ *    "numerical_contract" (block scale amax/6, clamp at 448, E2M1
+ *    round-to-nearest-even); benchmarks/gb10-cute-nvfp4-conversion-contract.json
+ *    (low nibble first packing).
+ *
+ * bf16 values travel as uint16_t bit patterns, e4m3 and packed e2m1 as
+ * uint8_t.  All arrays are contiguous, row-major.
+ */
+#ifndef ALNP_ORACLE_H
+#define ALNP_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats ---------------------------------------------------- */
+float    orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float f);
+double   orc_e4m3_decode(uint8_t code);
+uint8_t  orc_e4m3_encode_sat(float v);
+double   orc_e2m1_decode(uint8_t code);
+uint8_t  orc_e2m1_encode(float v);
+
+void orc_bf16_to_f32_n(const uint16_t* in, int64_t n, float* out);
+void orc_f32_to_bf16_n(const float* in, int64_t n, uint16_t* out);
+void orc_e4m3_decode_n(const uint8_t* in, int64_t n, double* out);
+void orc_e4m3_encode_sat_n(const float* in, int64_t n, uint8_t* out);
+void orc_e2m1_decode_n(const uint8_t* in, int64_t n, double* out);
+void orc_e2m1_encode_n(const float* in, int64_t n, uint8_t* out);
+
+/* ---- row statistics ---------------------------------------------------- */
+void orc_ln_stats(const uint16_t* x, int64_t rows, int64_t dim, float eps,
+                  float* mean, float* rstd);
+
+/* ---- FP8 producers ----------------------------------------------------- */
+/* y (nullable) receives the fp32 pre-quantization value, (rows, dim). */
+void orc_ln_fp8(const uint16_t* x, float act_scale, float eps, int64_t rows,
+                int64_t dim, uint8_t* out, float* mean, float* rstd, float* y);
+void orc_adaln_fp8_bcast(const uint16_t* x, const uint16_t* scale,
+                         const uint16_t* shift, float act_scale, float eps,
+                         int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                         float* rstd, float* y);
+void orc_adaln_fp8_ptok(const uint16_t* x, const uint16_t* scale,
+                        const uint16_t* shift, float act_scale, float eps,
+                        int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                        float* rstd, float* y);
+void orc_adaln_fp8_table(const uint16_t* x, const uint16_t* temb,
+                         const float* table, int64_t chunks, int64_t shift_idx,
+                         int64_t scale_idx, float act_scale, float eps,
+                         int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                         float* rstd, float* y);
+/* Per-token core fed fp32 operands directly, (rows, dim) each. */
+void orc_adaln_fp8_f32ops(const uint16_t* x, const float* scale,
+                          const float* shift, float act_scale, float eps,
+                          int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                          float* rstd, float* y);
+
+/* ---- FP4 producer ------------------------------------------------------ */
+/* One block of 16 values -> 16 e2m1 codes (4-bit, sign in bit 3) and one
+ * e4m3 block-scale code. */
+void orc_fp4_block_quant(const float* b, uint8_t* codes, uint8_t* scale_code);
+void orc_fp4_block_quant_n(const float* b, int64_t nblocks, uint8_t* codes,
+                           uint8_t* scale_codes);
+/* codes (n even, one per byte) -> n/2 bytes, element 2i in the low nibble. */
+void orc_fp4_pack(const uint8_t* codes, int64_t n, uint8_t* packed);
+/* b (nullable) receives the bf16-staged normalized row as fp32, (rows, dim). */
+void orc_ln_fp4(const uint16_t* x, float eps, int64_t rows, int64_t dim,
+                uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
+                float* b);
+
+/* ---- six-way modulation ------------------------------------------------ */
+/* params (tokens, 6, dim) fp32, mod (6, dim) fp32 -> out (6, tokens, dim)
+ * bf16 planes; plane k holds chunk k. */
+void orc_modulation6(const float* params, const float* mod, int64_t tokens,
+                     int64_t dim, uint16_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
