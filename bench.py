@@ -1,0 +1,318 @@
+"""Benchmark of the adaptive-LayerNorm producers on one MI355X.
+
+One step = one call of the per-token AdaLN -> FP8 producer (LayerNorm
+statistics, per-token modulation, static-scale e4m3 quantization: the whole
+FP8 hot path) at the Wan-video 2520 x 3072 shape the pages time, with inputs
+resident in HBM.  Headline: achieved algorithmic HBM GB/s (and us/call),
+timed COLD: consecutive steps rotate over enough input/output sets (>= 512 MB)
+that the 256 MB Infinity Cache cannot serve a step's operands from a previous
+step.  Launches are replayed from a HIP graph (the pages' graph method:
+several launches per graph, time / launches).
+
+The other producers (broadcast and table FP8, LN -> FP8, LN -> FP4,
+six-way modulation) are timed the same way at their workload sizes and
+reported under "rows"; the headline JSON line is the per-token FP8 one.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--only-headline] [--direct]
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+COLD_FOOTPRINT = 512 << 20     # 2x the Infinity Cache
+THOR_PTOK_US = 229.922         # pages: NVIDIA Thor, per-token M2520 D3072, raw op
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-headline", action="store_true",
+                   help="time only the per-token FP8 producer")
+    p.add_argument("--direct", action="store_true",
+                   help="launch each step directly instead of replaying a HIP graph")
+    return p.parse_args()
+
+
+# ---- workloads ----------------------------------------------------------------
+
+def algorithmic_bytes(name, d):
+    """Bytes a producer must move once: inputs read + outputs written."""
+    if name.startswith("modulation6"):
+        p = d["params"]
+        return p.nbytes + d["mod"].nbytes + p.size // 6 * 6 * 2
+    x = d["x"]
+    rows, dim = x.shape
+    if name.startswith("ln_fp4"):
+        return x.nbytes + rows * dim // 2 + rows * dim // 16
+    b = x.nbytes + rows * dim + 4  # x, e4m3 out, act_scale
+    if name.startswith("bcast") or name.startswith("ln_fp8"):
+        b += 0 if name.startswith("ln_fp8") else 2 * dim * 2
+    elif name.startswith("ptok"):
+        b += 2 * rows * dim * 2
+    elif name.startswith("table"):
+        b += 2 * rows * dim * 2 + 2 * dim * 4   # two temb chunks + two table rows
+    return b
+
+
+class Producer:
+    """Device buffers for `sets` copies of one workload and a raw C-ABI
+    launcher for set i (pointers precomputed: the step is the library call)."""
+
+    def __init__(self, name, d, sets, torch, alnp):
+        self.name, self.d, self.sets = name, d, sets
+        self.torch, self.L = torch, alnp.lib()
+        dev = torch.device("cuda")
+        bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+        self.keep = []
+        self.calls = []
+        kind = name.split("_")[0]
+        if kind == "modulation6":
+            p0, m0 = f32(d["params"]), f32(d["mod"])
+            B, S, _, D = p0.shape
+            for _ in range(sets):
+                p, m = p0.clone(), m0.clone()
+                outs = [torch.empty((B, S, D), dtype=torch.bfloat16, device=dev) for _ in range(6)]
+                arr = (ctypes.c_void_p * 6)(*[o.data_ptr() for o in outs])
+                self.keep += [p, m, outs, arr]
+                self.calls.append((self.L.alnp_adaln_modulation6_bf16,
+                                   (p.data_ptr(), m.data_ptr(), B, S, D, arr)))
+            self.outs = lambda i: self.keep[4 * i + 2]
+            return
+        x0 = bf(d["x"])
+        rows, dim = x0.shape
+        act0 = torch.tensor([d.get("act_scale", 0.025)], dtype=torch.float32, device=dev)
+        ops = {}
+        if kind in ("bcast", "ptok"):
+            ops = dict(scale=bf(d["scale"]), shift=bf(d["shift"]))
+        elif kind == "table":
+            ops = dict(temb=bf(d["temb"]), table=f32(d["table"]))
+        for _ in range(sets):
+            x, act = x0.clone(), act0.clone()
+            o = {k: v.clone() for k, v in ops.items()}
+            if kind == "fp4" or name.startswith("ln_fp4"):
+                packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=dev)
+                sf = torch.empty((rows, dim // 16), dtype=torch.uint8, device=dev)
+                self.keep.append((x, packed, sf))
+                self.calls.append((self.L.alnp_layer_norm_no_affine_quant_nvfp4_bf16,
+                                   (x.data_ptr(), d["eps"], rows, dim, packed.data_ptr(),
+                                    sf.data_ptr(), None, None)))
+                continue
+            out = torch.empty((rows, dim), dtype=torch.uint8, device=dev)
+            self.keep.append((x, act, o, out))
+            if kind == "ln":
+                self.calls.append((self.L.alnp_layer_norm_no_affine_quant_fp8_static_bf16,
+                                   (x.data_ptr(), act.data_ptr(), d["eps"], rows, dim,
+                                    out.data_ptr(), None, None)))
+            elif kind == "bcast":
+                self.calls.append((self.L.alnp_ada_layer_norm_quant_fp8_bf16,
+                                   (x.data_ptr(), o["scale"].data_ptr(), o["shift"].data_ptr(),
+                                    act.data_ptr(), d["eps"], rows, dim, out.data_ptr(),
+                                    None, None)))
+            elif kind == "ptok":
+                self.calls.append((self.L.alnp_ada_layer_norm_quant_fp8_ptok_bf16,
+                                   (x.data_ptr(), o["scale"].data_ptr(), o["shift"].data_ptr(),
+                                    act.data_ptr(), d["eps"], rows, dim, out.data_ptr(),
+                                    None, None)))
+            else:
+                chunks = d["temb"].shape[1]
+                self.calls.append((self.L.alnp_ada_layer_norm_quant_fp8_ptok_table_bf16,
+                                   (x.data_ptr(), o["temb"].data_ptr(), o["table"].data_ptr(),
+                                    chunks, d["shift_idx"], d["scale_idx"], act.data_ptr(),
+                                    d["eps"], rows, dim, out.data_ptr(), None, None)))
+
+    def launch(self, i, stream):
+        fn, args = self.calls[i % self.sets]
+        st = fn(*args, stream)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: status {st}")
+
+
+def sets_for(nbytes, cold):
+    return max(2, math.ceil(COLD_FOOTPRINT / nbytes)) if cold else 1
+
+
+def time_producer(prod, steps, warmup, use_graph, torch):
+    """Average us per step over exactly `steps` launches on the current
+    stream, measured with HIP events recorded on that stream."""
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for i in range(warmup):
+        prod.launch(i, h)
+    torch.cuda.synchronize()
+    graphs = []
+    if use_graph:
+        per = prod.sets
+        full, rem = divmod(steps, per)
+        cap = torch.cuda.Stream()
+        for n in ([per] if full else []) + ([rem] if rem else []):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                hh = torch.cuda.current_stream().cuda_stream
+                for i in range(n):
+                    prod.launch(i, hh)
+            graphs.append((g, n))
+        # Upload / first replay outside the timed region.
+        for g, _ in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        plan = [graphs[0][0]] * full if full else []
+        if rem:
+            plan.append(graphs[-1][0])
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    if use_graph:
+        for g in plan:
+            g.replay()
+    else:
+        for i in range(steps):
+            prod.launch(i, h)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1000.0 / steps
+
+
+# ---- counters from rocprofv3 (profiles/) --------------------------------------------
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---- CPU baseline -------------------------------------------------------------------------
+
+def cpu_baseline(d, nbytes):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = d["x"].shape[0]
+    oracle.adaln_fp8_ptok(d["x"][:8], d["scale"][:8], d["shift"][:8], 0.025)  # load
+    t = time.perf_counter()
+    oracle.adaln_fp8_ptok(d["x"], d["scale"], d["shift"], d["act_scale"], d["eps"], threads=threads)
+    dt = time.perf_counter() - t
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
+            "sample": f"the whole per-token 2520x3072 workload ({rows} rows), rows split "
+                      f"over {threads} threads, one pass, wall clock"}
+
+
+# ---- main -------------------------------------------------------------------------------------
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the producers are "
+                          "row-independent and would shard rows across GPUs with no "
+                          "exchange, but no multi-GPU path is built", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import dit_adaptive_layernorm_amd as alnp
+    from dit_adaptive_layernorm_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    use_graph = not a.direct
+
+    head = "ptok_fp8_2520x3072"
+    names = [head] if a.only_headline else [
+        head, "table_fp8_2520x3072", "bcast_fp8_16x2048", "ln_fp8_2520x3072",
+        "ln_fp4_4096x3072", "modulation6_1x5070x3072"]
+    results = {}
+    head_inputs = None
+    for name in names:
+        if name == "ln_fp8_2520x3072":
+            d = inputs.make("ln", rows=2520, dim=3072)
+        else:
+            d = inputs.workload(name)
+        if name == head:
+            head_inputs = d
+        nbytes = algorithmic_bytes(name, d)
+        r = {"bytes": nbytes}
+        for mode in ("cold", "warm"):
+            sets = sets_for(nbytes, mode == "cold")
+            prod = Producer(name, d, sets, torch, alnp)
+            us = time_producer(prod, a.steps, a.warmup, use_graph, torch)
+            r[mode] = {"us_per_call": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+                       "sets": sets, "footprint_mb": round(sets * nbytes / 2**20, 1)}
+            del prod
+            torch.cuda.empty_cache()
+        print(f"# {name}: cold {r['cold']['us_per_call']} us ({r['cold']['gbs']} GB/s), "
+              f"warm {r['warm']['us_per_call']} us", file=sys.stderr, flush=True)
+        results[name] = r
+
+    h = results[head]
+    us = h["cold"]["us_per_call"]
+    gbs = h["cold"]["gbs"]
+    traffic = measured_traffic(head)
+    line = {
+        "metric": "us/call and achieved HBM GB/s (% of peak) for AdaLN->FP8 at 2520x3072",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(THOR_PTOK_US / us, 3),
+        "vs_baseline_ref": "pages' NVIDIA Thor SM110a per-token M2520 D3072 raw op, 229.922 us "
+                           "(another machine; context only)",
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.1) per-token scale/shift, bf16)",
+        "config": {"workload": head, "rows": 2520, "dim": 3072, "act_scale": 0.025,
+                   "eps": 1e-5, "timing": "cold", "buffer_sets": h["cold"]["sets"],
+                   "footprint_mb": h["cold"]["footprint_mb"],
+                   "launch": "hipgraph" if use_graph else "direct"},
+        "us_per_call": us,
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "warm_us_per_call": h["warm"]["us_per_call"],
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_adaln_fp8_wave<6, per-token>",
+                     "algorithmic_bytes_per_launch": h["bytes"]},
+        "rows": {k: v for k, v in results.items() if k != head},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(head_inputs, h["bytes"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

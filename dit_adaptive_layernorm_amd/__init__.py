@@ -1,1 +1,256 @@
-"""placeholder"""
+"""Adaptive-LayerNorm producers for AMD MI355X (gfx950).
+
+A thin binding over libalnp.so, the HIP library built from csrc/ (C ABI in
+include/alnp.h).  The functions carry the names of the
+"adaptive-layernorm-producers" README ("Available Functions") and follow its
+"Tensor Contract": bf16 activations (rows, dim), broadcast / per-token /
+table modulation operands, an fp32 device scalar act_scale, FP8 e4m3 or
+packed FP4 e2m1 outputs, and optional caller-owned `out=` buffers for graph
+capture.
+
+This module only checks tensors and marshals pointers: every step runs in
+the HIP kernels, on the current torch stream.  If libalnp.so is missing or
+cannot be loaded the functions raise; there is no CPU fallback.
+
+Difference from the README: the FP4 entry takes its block scales in plain
+row-major (rows, dim // 16) order rather than the 128x4 swizzled layout; the
+function is named without "swizzled" and the buffer size comes from
+sf_size(rows, dim).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libalnp.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_I = ctypes.c_int
+
+# name -> (argtypes, restype); mirrors include/alnp.h.
+SIGNATURES = {
+    "alnp_abi_version": ([], _I),
+    "alnp_status_string": ([_I], ctypes.c_char_p),
+    "alnp_ada_layer_norm_quant_fp8_bf16": ([_P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_fp8_ptok_bf16": ([_P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_fp8_ptok_table_bf16": (
+        [_P, _P, _P, _I64, _I64, _I64, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_layer_norm_no_affine_quant_fp8_static_bf16": ([_P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_layer_norm_no_affine_quant_nvfp4_bf16": ([_P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_sf_size": ([_I64, _I64], _I64),
+    "alnp_adaln_modulation6_bf16": ([_P, _P, _I64, _I64, _I64, ctypes.POINTER(_P), _P], _I),
+    "alnp_quant_fp8_static_f32": ([_P, _P, _I64, _P, _P], _I),
+}
+
+STATUS = {0: "ALNP_OK", -1: "ALNP_ERR_NULL", -2: "ALNP_ERR_SHAPE", -3: "ALNP_ERR_DIM",
+          -4: "ALNP_ERR_INDEX", -5: "ALNP_ERR_ALIGN", -6: "ALNP_ERR_LAUNCH", -7: "ALNP_ERR_ARG"}
+
+_lib = None
+
+
+class AlnpError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({lib().alnp_status_string(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libalnp.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m dit_adaptive_layernorm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise AlnpError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, name, shape):
+    return None if t is None else _dev(t, name, torch.float32, shape)
+
+
+def _x(x):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, dim)")
+    _dev(x, "x", torch.bfloat16)
+    return x.shape
+
+
+def _act(act_scale):
+    if act_scale.numel() != 1:
+        raise ValueError("act_scale must hold one fp32 value")
+    return _dev(act_scale, "act_scale", torch.float32, act_scale.shape)
+
+
+def _fp8_out(out, x):
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    _dev(out, "out", torch.float8_e4m3fn, x.shape)
+    return out
+
+
+# ---- FP8 producers ----------------------------------------------------------
+
+def ada_layer_norm_quant_fp8_bf16(x, scale, shift, act_scale, eps=1e-5, out=None,
+                                  row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> FP8: scale, shift (dim,) bf16."""
+    rows, dim = _x(x)
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_fp8_bf16", lib().alnp_ada_layer_norm_quant_fp8_bf16(
+        x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (dim,)),
+        _dev(shift, "shift", torch.bfloat16, (dim,)), _act(act_scale), eps, rows, dim,
+        out.data_ptr(), _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+        _stream()))
+    return out
+
+
+def ada_layer_norm_quant_fp8_ptok_bf16(x, scale, shift, act_scale, eps=1e-5, out=None,
+                                       row_mean=None, row_rstd=None):
+    """Per-token AdaLN -> FP8: scale, shift (rows, dim) bf16."""
+    rows, dim = _x(x)
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_fp8_ptok_bf16", lib().alnp_ada_layer_norm_quant_fp8_ptok_bf16(
+        x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (rows, dim)),
+        _dev(shift, "shift", torch.bfloat16, (rows, dim)), _act(act_scale), eps, rows, dim,
+        out.data_ptr(), _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+        _stream()))
+    return out
+
+
+def ada_layer_norm_quant_fp8_ptok_table_bf16(x, temb, table, act_scale, shift_idx, scale_idx,
+                                             eps=1e-5, out=None, row_mean=None, row_rstd=None):
+    """Table-form per-token AdaLN -> FP8: temb (rows, chunks, dim) bf16, table
+    (chunks, dim) fp32; operands temb[:, idx] + table[idx]."""
+    rows, dim = _x(x)
+    if temb.dim() != 3:
+        raise ValueError("temb must be (rows, chunks, dim)")
+    chunks = temb.shape[1]
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_fp8_ptok_table_bf16",
+           lib().alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(
+               x.data_ptr(), _dev(temb, "temb", torch.bfloat16, (rows, chunks, dim)),
+               _dev(table, "table", torch.float32, (chunks, dim)), chunks, int(shift_idx),
+               int(scale_idx), _act(act_scale), eps, rows, dim, out.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return out
+
+
+def layer_norm_no_affine_quant_fp8_static_bf16(x, act_scale, eps=1e-5, out=None,
+                                               row_mean=None, row_rstd=None):
+    """LayerNorm (no affine) -> FP8."""
+    rows, dim = _x(x)
+    out = _fp8_out(out, x)
+    _check("alnp_layer_norm_no_affine_quant_fp8_static_bf16",
+           lib().alnp_layer_norm_no_affine_quant_fp8_static_bf16(
+               x.data_ptr(), _act(act_scale), eps, rows, dim, out.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return out
+
+
+# ---- FP4 producer ------------------------------------------------------------
+
+def sf_size(rows: int, dim: int) -> int:
+    """Bytes of the row-major e4m3 block-scale buffer: rows * dim // 16."""
+    n = lib().alnp_sf_size(rows, dim)
+    if n < 0:
+        raise AlnpError("alnp_sf_size", int(n))
+    return int(n)
+
+
+def layer_norm_no_affine_quant_nvfp4_bf16(x, eps=1e-5, packed=None, sf=None,
+                                          row_mean=None, row_rstd=None):
+    """LayerNorm (no affine) -> e2m1 packed (rows, dim // 2) uint8 (low nibble
+    first) + e4m3 block scales (rows, dim // 16), row-major."""
+    rows, dim = _x(x)
+    if dim % 16:
+        raise ValueError("dim must be a multiple of 16")
+    if packed is None:
+        packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rows, dim // 16), dtype=torch.float8_e4m3fn, device=x.device)
+    _dev(packed, "packed", torch.uint8, (rows, dim // 2))
+    if sf.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("sf must be uint8 or float8_e4m3fn")
+    _dev(sf, "sf", sf.dtype, (rows, dim // 16))
+    _check("alnp_layer_norm_no_affine_quant_nvfp4_bf16",
+           lib().alnp_layer_norm_no_affine_quant_nvfp4_bf16(
+               x.data_ptr(), eps, rows, dim, packed.data_ptr(), sf.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return packed, sf
+
+
+# ---- six-way modulation --------------------------------------------------------
+
+def adaln_modulation6_bf16(adaln_params, layer_modulation, out=None):
+    """fp32 (batch, seq, 6, dim) + fp32 (6, dim) -> six bf16 (batch, seq, dim)."""
+    if adaln_params.dim() != 4 or adaln_params.shape[2] != 6:
+        raise ValueError("adaln_params must be (batch, seq, 6, dim)")
+    B, S, _, D = adaln_params.shape
+    _dev(adaln_params, "adaln_params", torch.float32)
+    _dev(layer_modulation, "layer_modulation", torch.float32, (6, D))
+    if out is None:
+        out = [torch.empty((B, S, D), dtype=torch.bfloat16, device=adaln_params.device)
+               for _ in range(6)]
+    if len(out) != 6:
+        raise ValueError("out must hold six tensors")
+    ptrs = (_P * 6)(*[_dev(o, f"out[{k}]", torch.bfloat16, (B, S, D)) for k, o in enumerate(out)])
+    _check("alnp_adaln_modulation6_bf16", lib().alnp_adaln_modulation6_bf16(
+        adaln_params.data_ptr(), layer_modulation.data_ptr(), B, S, D, ptrs, _stream()))
+    return tuple(out)
+
+
+# ---- standalone quantizer --------------------------------------------------------
+
+def quant_fp8_static_f32(v, act_scale, out=None):
+    """e4m3(v * (1 / act_scale)), saturating; v fp32 of any shape."""
+    _dev(v, "v", torch.float32)
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.float8_e4m3fn, device=v.device)
+    _dev(out, "out", torch.float8_e4m3fn, v.shape)
+    _check("alnp_quant_fp8_static_f32", lib().alnp_quant_fp8_static_f32(
+        v.data_ptr(), _act(act_scale), v.numel(), out.data_ptr(), _stream()))
+    return out
+
+
+__all__ = [
+    "ada_layer_norm_quant_fp8_bf16", "ada_layer_norm_quant_fp8_ptok_bf16",
+    "ada_layer_norm_quant_fp8_ptok_table_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
+    "layer_norm_no_affine_quant_nvfp4_bf16", "sf_size", "adaln_modulation6_bf16",
+    "quant_fp8_static_f32", "lib", "AlnpError", "SIGNATURES",
+]

@@ -1,0 +1,65 @@
+"""Build libalnp.so (the HIP producers and their C ABI) for gfx950 in-tree.
+
+    python -m dit_adaptive_layernorm_amd.build      # or build() from Python
+
+Every call recompiles.  Flags: -O3; -ffp-contract=off so that the modulation
+and quantization arithmetic is evaluated exactly in the written order
+(explicit __builtin_fmaf only in the variance accumulation); packed-fp32
+instructions disabled in the device code generator.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libalnp.so")
+SOURCES = ["producers.hip", "modulation6.hip", "abi.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # The host compiler pass warns that it does not know the packed-fp32
+    # feature; that is expected.  Show anything else.
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+
+
+def build(verbose: bool = False, jobs: int = 3) -> str:
+    with tempfile.TemporaryDirectory(prefix="alnp_build_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            objs.append(obj)
+            procs.append((src, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        # Compile the translation units in parallel.
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max(1, jobs)) as ex:
+            list(ex.map(lambda p: _run(p[1], verbose), procs))
+        tmp_lib = LIB + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,203 @@
+// abi.hip -- the C entry points of libalnp: host-side validation, then one
+// kernel launch on the caller's stream.  Nothing here allocates, frees or
+// synchronizes.  Argument conventions and error codes are documented in
+// include/alnp.h.
+#include "alnp.h"
+#include "kernels.hpp"
+
+#include <cmath>
+
+namespace {
+
+using alnp::Fp4Args;
+using alnp::Fp8Args;
+using alnp::Mod6Args;
+
+constexpr int64_t kMaxRows = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxQuantN = int64_t(1) << 31;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? ALNP_OK : ALNP_ERR_LAUNCH; }
+
+// Checks shared by the LayerNorm producers.  Returns ALNP_OK to go on, or a
+// status to return (1 = valid no-op for rows == 0).
+int check_rows_dim(int64_t rows, int64_t dim, int64_t dim_multiple)
+{
+    if (rows < 0 || rows > kMaxRows || dim <= 0 || dim > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (dim % dim_multiple != 0)
+        return ALNP_ERR_DIM;
+    return rows == 0 ? 1 : ALNP_OK;
+}
+
+int check_eps(float eps) { return (std::isfinite(eps) && eps >= 0.f) ? ALNP_OK : ALNP_ERR_ARG; }
+
+// Common tail of the FP8 producers: null/alignment/eps checks, choice of
+// kernel, launch.
+int run_fp8(Fp8Args a, int form, void* stream)
+{
+    if (!a.x || !a.act_scale || !a.out)
+        return ALNP_ERR_NULL;
+    if ((form == 1 || form == 2) && (!a.scale || !a.shift))
+        return ALNP_ERR_NULL;
+    if (form == 3 && (!a.temb || !a.table))
+        return ALNP_ERR_NULL;
+    if (!aligned(a.x, 2) || !aligned(a.act_scale, 4) || !aligned(a.scale, 2) ||
+        !aligned(a.shift, 2) || !aligned(a.temb, 2) || !aligned(a.table, 4) ||
+        !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
+        return ALNP_ERR_ALIGN;
+    if (int st = check_eps(a.eps))
+        return st;
+    const bool fast = a.dim % 8 == 0 && a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) &&
+                      aligned(a.scale, 16) && aligned(a.shift, 16) && aligned(a.temb, 16) &&
+                      aligned(a.table, 16) && aligned(a.out, 8);
+    return launch_status(alnp::launch_adaln_fp8(a, form, fast, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int alnp_abi_version(void) { return 1; }
+
+const char* alnp_status_string(int status)
+{
+    switch (status) {
+    case ALNP_OK: return "ok";
+    case ALNP_ERR_NULL: return "a required pointer is NULL";
+    case ALNP_ERR_SHAPE: return "rows/dim out of range";
+    case ALNP_ERR_DIM: return "dim must be even (FP8) or a multiple of 16 (FP4)";
+    case ALNP_ERR_INDEX: return "chunk index outside [0, chunks)";
+    case ALNP_ERR_ALIGN: return "pointer not aligned to its element size";
+    case ALNP_ERR_LAUNCH: return "kernel launch failed";
+    case ALNP_ERR_ARG: return "eps must be finite and >= 0";
+    default: return "unknown status";
+    }
+}
+
+int alnp_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                       const uint16_t* shift, const float* act_scale, float eps,
+                                       int64_t rows, int64_t dim, uint8_t* out, float* row_mean,
+                                       float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    Fp8Args a{x, scale, shift, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
+              out, row_mean, row_rstd};
+    return run_fp8(a, 1, stream);
+}
+
+int alnp_ada_layer_norm_quant_fp8_ptok_bf16(const uint16_t* x, const uint16_t* scale,
+                                            const uint16_t* shift, const float* act_scale,
+                                            float eps, int64_t rows, int64_t dim, uint8_t* out,
+                                            float* row_mean, float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    Fp8Args a{x, scale, shift, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
+              out, row_mean, row_rstd};
+    return run_fp8(a, 2, stream);
+}
+
+int alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(const uint16_t* x, const uint16_t* temb,
+                                                  const float* table, int64_t chunks,
+                                                  int64_t shift_idx, int64_t scale_idx,
+                                                  const float* act_scale, float eps, int64_t rows,
+                                                  int64_t dim, uint8_t* out, float* row_mean,
+                                                  float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    if (chunks <= 0 || chunks > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (shift_idx < 0 || shift_idx >= chunks || scale_idx < 0 || scale_idx >= chunks)
+        return ALNP_ERR_INDEX;
+    Fp8Args a{x, nullptr, nullptr, temb, table, chunks, shift_idx, scale_idx, act_scale, eps,
+              rows, (int)dim, out, row_mean, row_rstd};
+    return run_fp8(a, 3, stream);
+}
+
+int alnp_layer_norm_no_affine_quant_fp8_static_bf16(const uint16_t* x, const float* act_scale,
+                                                    float eps, int64_t rows, int64_t dim,
+                                                    uint8_t* out, float* row_mean,
+                                                    float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    Fp8Args a{x, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
+              out, row_mean, row_rstd};
+    return run_fp8(a, 0, stream);
+}
+
+int alnp_layer_norm_no_affine_quant_nvfp4_bf16(const uint16_t* x, float eps, int64_t rows,
+                                               int64_t dim, uint8_t* packed, uint8_t* sf,
+                                               float* row_mean, float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 16))
+        return st > 0 ? ALNP_OK : st;
+    if (!x || !packed || !sf)
+        return ALNP_ERR_NULL;
+    if (!aligned(x, 2) || !aligned(row_mean, 4) || !aligned(row_rstd, 4))
+        return ALNP_ERR_ALIGN;
+    if (int st = check_eps(eps))
+        return st;
+    Fp4Args a{x, eps, rows, (int)dim, packed, sf, row_mean, row_rstd};
+    const bool fast = dim <= alnp::kMaxFastDim && aligned(x, 16) && aligned(packed, 4);
+    return launch_status(alnp::launch_ln_fp4(a, fast, as_stream(stream)));
+}
+
+int64_t alnp_sf_size(int64_t rows, int64_t dim)
+{
+    if (rows < 0 || rows > kMaxRows || dim <= 0 || dim > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (dim % 16 != 0)
+        return ALNP_ERR_DIM;
+    return rows * (dim / 16);
+}
+
+int alnp_adaln_modulation6_bf16(const float* params, const float* layer_mod, int64_t batch,
+                                int64_t seq, int64_t dim, uint16_t* const out[6], void* stream)
+{
+    if (batch < 0 || seq < 0 || dim <= 0 || dim > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (seq != 0 && batch > kMaxRows / seq)
+        return ALNP_ERR_SHAPE;
+    const int64_t tokens = batch * seq;
+    if (tokens == 0)
+        return ALNP_OK;
+    if (!params || !layer_mod || !out)
+        return ALNP_ERR_NULL;
+    Mod6Args a{params, layer_mod, tokens, (int)dim, {}};
+    bool fast = dim % 8 == 0 && aligned(params, 16) && aligned(layer_mod, 16);
+    for (int k = 0; k < 6; ++k) {
+        if (!out[k])
+            return ALNP_ERR_NULL;
+        if (!aligned(out[k], 2))
+            return ALNP_ERR_ALIGN;
+        fast = fast && aligned(out[k], 16);
+        a.out[k] = out[k];
+    }
+    if (!aligned(params, 4) || !aligned(layer_mod, 4))
+        return ALNP_ERR_ALIGN;
+    return launch_status(alnp::launch_modulation6(a, fast, as_stream(stream)));
+}
+
+int alnp_quant_fp8_static_f32(const float* v, const float* act_scale, int64_t n, uint8_t* out,
+                              void* stream)
+{
+    if (n < 0 || n > kMaxQuantN)
+        return ALNP_ERR_SHAPE;
+    if (n == 0)
+        return ALNP_OK;
+    if (!v || !act_scale || !out)
+        return ALNP_ERR_NULL;
+    if (!aligned(v, 4) || !aligned(act_scale, 4))
+        return ALNP_ERR_ALIGN;
+    return launch_status(alnp::launch_quant_fp8(v, act_scale, n, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// device_common.hpp -- gfx950 device helpers shared by the producer kernels.
+//
+// Compiled with -ffp-contract=off: every float expression below is one
+// IEEE-rounded operation unless it calls __builtin_fmaf explicitly, so the
+// modulation order (xhat * (1 + scale)) + shift is evaluated exactly as
+// written.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace alnp {
+
+constexpr int kWave = 64;
+
+// ---- bf16 ----------------------------------------------------------------
+
+// bf16 -> fp32 is exact: the pattern is the upper half of the float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight bf16 (one 16-byte vector) -> eight floats.
+__device__ __forceinline__ void unpack8(const uint4& v, float f[8])
+{
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16, round to nearest even (v_cvt_pk_bf16_f32);
+// element a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ---- e4m3 ----------------------------------------------------------------
+
+// Clamp to the e4m3 range, keeping NaN (the comparison is false for NaN).
+__device__ __forceinline__ float sat448(float v)
+{
+    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+
+// Four floats (already in range) -> four e4m3 codes, element a in byte 0.
+// v_cvt_pk_fp8_f32 rounds to nearest even and writes the OCP e4m3 format on
+// gfx950.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Value of a non-negative e4m3 code below 0x7F: m * 2^-9 (subnormal) or
+// (8 + m) * 2^(e - 10).
+__device__ __forceinline__ float e4m3_value(uint32_t code)
+{
+    uint32_t e = (code >> 3) & 0xF, m = code & 7;
+    return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8 + m), (int)e - 10);
+}
+
+// ---- e2m1 ----------------------------------------------------------------
+
+// Round to nearest even onto {0, .5, 1, 1.5, 2, 3, 4, 6}: count the decision
+// points passed.  Strict '>' at points whose lower neighbour has the even
+// code, '>=' where the upper one does; 6 and above (and inf) give code 7.
+// NaN passes no point and keeps only its sign.
+__device__ __forceinline__ uint32_t e2m1_code(float v)
+{
+    float a = fabsf(v);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                 (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// ---- wave reductions ------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes; every lane gets the same bits.  DPP butterflies
+// inside each row of 16 lanes (xor 1, xor 2, half-mirror, mirror: each lane
+// adds the same two operands as its partner, so partners hold identical
+// sums), then the four row sums are combined in a fixed order from lanes 0,
+// 16, 32 and 48.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = v + dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = v + dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = v + dpp<0x141>(v);   // row_half_mirror
+    v = v + dpp<0x140>(v);   // row_mirror
+    float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
+// Max of a lane and its xor-1 partner (the two lanes holding one 16-element
+// FP4 block).
+__device__ __forceinline__ float pair_max(float v)
+{
+    return fmaxf(v, dpp<0xB1>(v));
+}
+
+}  // namespace alnp

@@ -1,0 +1,186 @@
+/*
+ * alnp.h -- C ABI of the adaptive-LayerNorm producers for AMD MI355X (gfx950).
+ *
+ * The producers fuse the work in front of a low-precision GEMM in a DiT /
+ * Wan-style block: per row of a bf16 (rows, dim) activation, LayerNorm
+ * without affine weights, the DiT modulation xhat * (1 + scale) + shift, and
+ * quantization to FP8 e4m3 (static scale) or FP4 e2m1 (e4m3 scale per 16
+ * elements); plus the six-way modulation producer.  Sources: the
+ * "adaptive-layernorm-producers" README ("Available Functions", "Tensor
+ * Contract", "Minimal Usage") and its "Benchmark Results" page.
+ *
+ * Conventions shared by every entry point
+ *  - Types: bf16 tensors are passed as uint16_t bit patterns, e4m3 and
+ *    packed e2m1 as uint8_t, fp32 as float.  All tensors are contiguous and
+ *    row-major; pointers are DEVICE pointers unless a parameter says
+ *    otherwise.
+ *  - Ownership: the caller allocates every buffer and keeps it alive until
+ *    the work queued on `stream` has finished.  The library never allocates,
+ *    frees or synchronizes; each call validates its arguments on the host,
+ *    enqueues one kernel on `stream` (a hipStream_t; NULL is the null stream)
+ *    and returns.  Calls can be captured into a HIP graph.
+ *  - Errors: a negative status is returned and NOTHING is launched (outputs
+ *    untouched) for: a NULL required pointer (ALNP_ERR_NULL); rows < 0,
+ *    dim <= 0 or sizes past the limits below (ALNP_ERR_SHAPE); dim odd for
+ *    FP8 or not a multiple of 16 for FP4 (ALNP_ERR_DIM); a chunk index
+ *    outside [0, chunks) (ALNP_ERR_INDEX); a pointer not aligned to its
+ *    element size (ALNP_ERR_ALIGN); a negative or non-finite eps
+ *    (ALNP_ERR_ARG).  rows == 0 is a valid no-op.  If the launch itself
+ *    fails, ALNP_ERR_LAUNCH is returned.  Device scalars (act_scale) are not
+ *    inspected on the host.
+ *  - Aliasing: outputs must not overlap inputs or each other.
+ *  - Limits: rows (and batch * seq) <= 2^24 - 1; dim <= 2^24;
+ *    alnp_quant_fp8_static_f32 takes n <= 2^31.
+ *  - Numerics (identical for every operand form):
+ *      mean = sum(x) / dim, var = sum((x - mean)^2) / dim   (fp32, biased)
+ *      rstd = 1 / sqrt(var + eps)
+ *      xhat = (x - mean) * rstd
+ *      y    = (xhat * (1 + scale)) + shift   (fp32, each op rounded,
+ *                                             no fused multiply-add)
+ *      q    = e4m3(y * (1 / act_scale))     (round to nearest even,
+ *                                             saturating at +-448; a NaN
+ *                                             gives a NaN code, 0x7F or
+ *                                             0xFF: the sign is not kept)
+ *    The operation order (x * (scale + 1)) + shift is the one the
+ *    h3-blackwell-runtime page states ("NVFP4 Modulation Producer Fusion",
+ *    "Exactness Contract").
+ *  - Optional outputs row_mean / row_rstd (fp32, (rows,)) receive the row
+ *    statistics when non-NULL.
+ */
+#ifndef ALNP_H
+#define ALNP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum alnp_status {
+    ALNP_OK = 0,
+    ALNP_ERR_NULL = -1,
+    ALNP_ERR_SHAPE = -2,
+    ALNP_ERR_DIM = -3,
+    ALNP_ERR_INDEX = -4,
+    ALNP_ERR_ALIGN = -5,
+    ALNP_ERR_LAUNCH = -6,
+    ALNP_ERR_ARG = -7
+};
+
+/* Version of this ABI; bumped on any signature change. */
+int alnp_abi_version(void);
+
+/* Static string for a status code; never NULL. */
+const char* alnp_status_string(int status);
+
+/*
+ * Broadcast AdaLN -> FP8 (README "Available Functions":
+ * ada_layer_norm_quant_fp8_bf16; "Tensor Contract": broadcast scale/shift).
+ *   x          (rows, dim) bf16
+ *   scale      (dim,) bf16, shared by every row
+ *   shift      (dim,) bf16, shared by every row
+ *   act_scale  device fp32 scalar, the dequantization scale
+ *   eps        LayerNorm epsilon (the pages use 1e-5)
+ *   out        (rows, dim) e4m3 codes
+ *   row_mean, row_rstd  optional (rows,) fp32
+ * dim must be even.
+ */
+int alnp_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                       const uint16_t* shift,
+                                       const float* act_scale, float eps,
+                                       int64_t rows, int64_t dim, uint8_t* out,
+                                       float* row_mean, float* row_rstd,
+                                       void* stream);
+
+/*
+ * Per-token AdaLN -> FP8 (README: ada_layer_norm_quant_fp8_ptok_bf16,
+ * "per-token modulation without materializing a broadcast buffer").
+ *   scale, shift  (rows, dim) bf16, one row of operands per activation row.
+ * Other arguments as for the broadcast form.
+ */
+int alnp_ada_layer_norm_quant_fp8_ptok_bf16(const uint16_t* x,
+                                            const uint16_t* scale,
+                                            const uint16_t* shift,
+                                            const float* act_scale, float eps,
+                                            int64_t rows, int64_t dim,
+                                            uint8_t* out, float* row_mean,
+                                            float* row_rstd, void* stream);
+
+/*
+ * Table-form per-token AdaLN -> FP8 (README:
+ * ada_layer_norm_quant_fp8_ptok_table_bf16, "fused host modulation table add
+ * and chunk selection").
+ *   temb       (rows, chunks, dim) bf16
+ *   table      (chunks, dim) fp32
+ *   shift_idx, scale_idx  chunk indices in [0, chunks); they may be equal
+ * The operands are scale[r, j] = temb[r, scale_idx, j] + table[scale_idx, j]
+ * and likewise shift, each one fp32 addition (not rounded to bf16).  Only the
+ * two selected chunks of temb are read.
+ */
+int alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(
+    const uint16_t* x, const uint16_t* temb, const float* table, int64_t chunks,
+    int64_t shift_idx, int64_t scale_idx, const float* act_scale, float eps,
+    int64_t rows, int64_t dim, uint8_t* out, float* row_mean, float* row_rstd,
+    void* stream);
+
+/*
+ * LayerNorm (no affine) -> FP8 (README:
+ * layer_norm_no_affine_quant_fp8_static_bf16).  Same arithmetic as the
+ * AdaLN forms with scale = shift = 0, so the result equals the broadcast
+ * form called with zero operands, bit for bit.
+ */
+int alnp_layer_norm_no_affine_quant_fp8_static_bf16(
+    const uint16_t* x, const float* act_scale, float eps, int64_t rows,
+    int64_t dim, uint8_t* out, float* row_mean, float* row_rstd, void* stream);
+
+/*
+ * LayerNorm (no affine) -> FP4 (README:
+ * layer_norm_no_affine_quant_nvfp4_swizzled_bf16, with the block scales in
+ * plain row-major order instead of the 128x4 swizzle).
+ *   packed  (rows, dim/2) uint8: two e2m1 codes per byte, element 2i in the
+ *           low nibble (low-nibble-first, as the conversion-contract example
+ *           on the h3-blackwell-runtime page prints)
+ *   sf      (rows, dim/16) e4m3 block scales, row-major; size from
+ *           alnp_sf_size()
+ * Per row: xhat as above, rounded to bf16 (the README's staged BF16 norm);
+ * per block of 16: s = e4m3(amax / 6) (IEEE division, saturating at 448);
+ * codes = e2m1(b * (1 / s)) rounded to nearest even, saturating at +-6; a
+ * block whose scale is 0 gets all-zero codes.  dim % 16 == 0.
+ */
+int alnp_layer_norm_no_affine_quant_nvfp4_bf16(const uint16_t* x, float eps,
+                                               int64_t rows, int64_t dim,
+                                               uint8_t* packed, uint8_t* sf,
+                                               float* row_mean,
+                                               float* row_rstd, void* stream);
+
+/* Bytes of the row-major block-scale buffer for an FP4 output: rows*dim/16.
+ * Returns a negative status for invalid sizes. */
+int64_t alnp_sf_size(int64_t rows, int64_t dim);
+
+/*
+ * Six-way DiT modulation (README: adaln_modulation6_bf16; "Tensor Contract":
+ * FP32 (batch, sequence, 6, dim) parameters plus FP32 (6, dim) layer
+ * modulation, six BF16 (batch, sequence, dim) outputs).
+ *   params     (batch, seq, 6, dim) fp32
+ *   layer_mod  (6, dim) fp32
+ *   out        HOST array of 6 device pointers; out[k] is (batch, seq, dim)
+ *              bf16 and receives bf16_rne(params[b, s, k, :] + layer_mod[k, :])
+ * NaN sums give a quiet NaN, overflow gives +-inf.
+ */
+int alnp_adaln_modulation6_bf16(const float* params, const float* layer_mod,
+                                int64_t batch, int64_t seq, int64_t dim,
+                                uint16_t* const out[6], void* stream);
+
+/*
+ * Static-scale FP8 quantizer on its own, the last stage of every FP8
+ * producer: out[i] = e4m3(v[i] * (1 / act_scale)), same rounding and
+ * saturation as above.  n >= 0 elements of fp32 input.
+ */
+int alnp_quant_fp8_static_f32(const float* v, const float* act_scale,
+                              int64_t n, uint8_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ALNP_H */
