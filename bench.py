@@ -36,19 +36,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_FOOTPRINT = 512 << 20     # 2x the Infinity Cache
+COPY_BYTES = 256 << 20         # plain copy used to scale the rocprofv3 byte counters
 THOR_PTOK_US = 229.922         # pages: NVIDIA Thor, per-token M2520 D3072, raw op
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-headline", action="store_true",
                    help="time only the per-token FP8 producer")
     p.add_argument("--direct", action="store_true",
                    help="launch each step directly instead of replaying a HIP graph")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run four plain device copies of 256 MiB (reference for "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
     return p.parse_args()
 
 
@@ -151,45 +155,37 @@ def sets_for(nbytes, cold):
     return max(2, math.ceil(COLD_FOOTPRINT / nbytes)) if cold else 1
 
 
-def time_producer(prod, steps, warmup, use_graph, torch):
-    """Average us per step over exactly `steps` launches on the current
-    stream, measured with HIP events recorded on that stream."""
-    stream = torch.cuda.current_stream()
+def time_producer(prod, steps, warmup, use_graph, torch, stream):
+    """Average us per step over exactly `steps` launches on `stream` (a
+    dedicated stream, as a pipeline would use), measured with HIP events
+    recorded on that stream.  With a graph, the `steps` launches are captured
+    once and the graph is replayed once untimed (upload) before the timed
+    replay."""
     h = stream.cuda_stream
-    for i in range(warmup):
-        prod.launch(i, h)
-    torch.cuda.synchronize()
-    graphs = []
-    if use_graph:
-        per = prod.sets
-        full, rem = divmod(steps, per)
-        cap = torch.cuda.Stream()
-        for n in ([per] if full else []) + ([rem] if rem else []):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                hh = torch.cuda.current_stream().cuda_stream
-                for i in range(n):
-                    prod.launch(i, hh)
-            graphs.append((g, n))
-        # Upload / first replay outside the timed region.
-        for g, _ in graphs:
-            g.replay()
-        torch.cuda.synchronize()
-        plan = [graphs[0][0]] * full if full else []
-        if rem:
-            plan.append(graphs[-1][0])
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    if use_graph:
-        for g in plan:
-            g.replay()
-    else:
-        for i in range(steps):
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
             prod.launch(i, h)
-    t1.record(stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        g = None
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                hh = torch.cuda.current_stream().cuda_stream
+                for i in range(steps):
+                    prod.launch(i, hh)
+            g.replay()
+            torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        if use_graph:
+            g.replay()
+        else:
+            for i in range(steps):
+                prod.launch(i, h)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    del g
     return t0.elapsed_time(t1) * 1000.0 / steps
 
 
@@ -249,6 +245,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     use_graph = not a.direct
+    if a.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "copies": 4}))
+        return
 
     head = "ptok_fp8_2520x3072"
     names = [head] if a.only_headline else [
@@ -256,6 +260,7 @@ def main():
         "ln_fp4_4096x3072", "modulation6_1x5070x3072"]
     results = {}
     head_inputs = None
+    stream = torch.cuda.Stream()
     for name in names:
         if name == "ln_fp8_2520x3072":
             d = inputs.make("ln", rows=2520, dim=3072)
@@ -268,7 +273,7 @@ def main():
         for mode in ("cold", "warm"):
             sets = sets_for(nbytes, mode == "cold")
             prod = Producer(name, d, sets, torch, alnp)
-            us = time_producer(prod, a.steps, a.warmup, use_graph, torch)
+            us = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream)
             r[mode] = {"us_per_call": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
                        "sets": sets, "footprint_mb": round(sets * nbytes / 2**20, 1)}
             del prod
@@ -305,7 +310,7 @@ def main():
         "warm_us_per_call": h["warm"]["us_per_call"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_adaln_fp8_wave<6, per-token>",
+                     "kernel": "k_adaln_fp8_rows<3 vectors/thread, 2 waves, per-token>",
                      "algorithmic_bytes_per_launch": h["bytes"]},
         "rows": {k: v for k, v in results.items() if k != head},
     }

@@ -13,6 +13,38 @@ namespace alnp {
 
 constexpr int kWave = 64;
 
+// ---- memory ----------------------------------------------------------------
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte loads.  Streamed operands (read once per call) use the
+// non-temporal hint so they do not displace reused data in L2 / Infinity
+// Cache; operands shared by every row (broadcast scale/shift, the table) use
+// ordinary loads.
+__device__ __forceinline__ uint4 ld_stream(const void* p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_keep(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Non-temporal stores of 4, 8 and 16 bytes (outputs are not re-read here).
+__device__ __forceinline__ void st_stream(void* p, uint32_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, uint2 v)
+{
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, uint4 v)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // ---- bf16 ----------------------------------------------------------------
 
 // bf16 -> fp32 is exact: the pattern is the upper half of the float.
@@ -103,6 +135,24 @@ __device__ __forceinline__ float wave_sum(float v)
     float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
     return (a + b) + (c + d);
+}
+
+// Sum over the waves of a workgroup (nwaves <= 16), same bits in every
+// thread: wave sums, then the per-wave partials added in wave order.  `slot`
+// is LDS for 16 floats; the trailing barrier is left to the caller's next
+// use of the slot.
+__device__ __forceinline__ float group_sum(float v, float* slot, int nwaves)
+{
+    v = wave_sum(v);
+    if (nwaves == 1)
+        return v;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        slot[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = slot[0];
+    for (int k = 1; k < nwaves; ++k)
+        r += slot[k];
+    return r;
 }
 
 // Max of a lane and its xor-1 partner (the two lanes holding one 16-element

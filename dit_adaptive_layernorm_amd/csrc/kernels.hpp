@@ -44,12 +44,20 @@ struct Mod6Args {
     uint16_t* out[6];
 };
 
-// Largest row (elements) the register-resident wave-per-row kernels take:
-// 16 vectors of 8 per lane.
-constexpr int kMaxFastDim = 16 * 8 * 64;
+// Largest row (elements) the register-resident row kernels take: 8 waves,
+// 8 vectors of 8 elements per thread.
+constexpr int kMaxFastDim = 8 * 64 * 8 * 8;
+
+// Launch shape of the row kernels for a row of dim elements (dim % 8 == 0,
+// dim <= kMaxFastDim): threads per workgroup and 16-byte vectors per thread.
+struct RowShape {
+    int threads;
+    int vpt;
+};
+RowShape row_shape(int dim);
 
 // form: 0 LayerNorm only, 1 broadcast, 2 per-token, 3 table.
-// fast: wave-per-row kernel (dim % 8 == 0, dim <= kMaxFastDim, operands
+// fast: row kernel (dim % 8 == 0, dim <= kMaxFastDim, operands
 // 16-byte aligned); otherwise the workgroup-per-row kernel.
 hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s);
 hipError_t launch_ln_fp4(const Fp4Args& a, bool fast, hipStream_t s);

@@ -9,17 +9,25 @@
 //
 // Kernel design (MI355X): the problem is a pure stream (3-7 bytes moved per
 // element, ~15 flops), so the kernels are built for HBM, not MFMA.
-//  - Fast path: one wave64 per row, four rows per 256-thread workgroup.  A
-//    lane owns NV 16-byte vectors of the row (vector i = v*64 + lane), so
-//    every load instruction of a wave covers 1 KiB of contiguous memory.
-//    The whole row stays in registers: x, then the per-token operands, are
-//    requested up front so their latency overlaps; mean and variance are two
-//    passes over registers with DPP wave reductions (no LDS, no barrier).
-//  - Fallback (dim not a multiple of 8, rows longer than 8192, or operands
-//    not 16-byte aligned): one 256-thread workgroup per row, element loops,
-//    LDS for the cross-wave sums.  Same arithmetic.
+//  - Fast path: one workgroup per row, 1, 2, 4 or 8 waves (a template
+//    parameter, so launch bounds and indexing are compile-time), each thread
+//    holding VPT
+//    16-byte vectors of the row (vector i = v * threads + t), so every load
+//    instruction of a wave covers 1 KiB of contiguous memory.  For dim 3072:
+//    two waves, three vectors per thread.  The row stays in registers: x,
+//    then the per-token operands, are requested up front so their latency
+//    overlaps; mean and variance are two passes over registers with DPP wave
+//    reductions and one LDS exchange between the waves.  Spreading a row over
+//    several waves keeps the serial arithmetic each wave does after its data
+//    arrives short, which is what bounds the end of the kernel.  Streamed
+//    operands use non-temporal loads and the outputs non-temporal stores.
+//  - Fallback (dim not a multiple of 8, rows longer than 32768, or operands
+//    not 16-byte aligned): one 256-thread workgroup per row, element loops.
+//    Same arithmetic.
 #include "device_common.hpp"
 #include "kernels.hpp"
+
+#include <algorithm>
 
 namespace alnp {
 
@@ -36,33 +44,38 @@ __device__ __forceinline__ void load_f32x8(const float* p, float f[8])
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// ---- fast path: one wave per row --------------------------------------------
+// ---- fast path: one workgroup per row, row held in registers ---------------
 
-// Loads vector i of a bf16 row, or zeros past the end of the row.
-__device__ __forceinline__ uint4 ld16(const uint16_t* row, int i, int nvec)
+// Vector i of a row (eight elements), or zeros past the row end.
+template <bool STREAM>
+__device__ __forceinline__ uint4 ld_row(const uint16_t* row, int i, int nvec)
 {
-    return i < nvec ? reinterpret_cast<const uint4*>(row)[i] : make_uint4(0, 0, 0, 0);
+    if (i >= nvec)
+        return make_uint4(0, 0, 0, 0);
+    return STREAM ? ld_stream(row + 8 * i) : ld_keep(row + 8 * i);
 }
 
-// Row statistics from the NV register vectors of a lane.  Zero-filled
-// vectors past the row end add nothing to the sum and are skipped in the
-// squared deviations.
-template <int NV>
-__device__ __forceinline__ void row_stats(const uint4 (&xv)[NV], int lane, int nvec, int dim,
-                                          float eps, float& mean, float& rstd)
+// Row statistics from a thread's VPT register vectors (vector v of thread t is
+// row vector v * nthreads + t).  Zero vectors past the row end add nothing to
+// the sum and are skipped in the squared deviations.
+template <int VPT, int WAVES>
+__device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], int nvec, int dim, float eps,
+                                          float* red, float& mean, float& rstd)
 {
+    constexpr int nwaves = WAVES;
+    constexpr int nthreads = WAVES * kWave;
     float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
+    for (int v = 0; v < VPT; ++v) {
         float f[8];
         unpack8(xv[v], f);
         s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
     }
-    mean = wave_sum(s) / (float)dim;
+    mean = group_sum(s, red, nwaves) / (float)dim;
     float q = 0.f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        if (v * kWave + lane < nvec) {
+    for (int v = 0; v < VPT; ++v) {
+        if (v * nthreads + (int)threadIdx.x < nvec) {
             float f[8];
             unpack8(xv[v], f);
 #pragma unroll
@@ -72,151 +85,160 @@ __device__ __forceinline__ void row_stats(const uint4 (&xv)[NV], int lane, int n
             }
         }
     }
-    const float var = wave_sum(q) / (float)dim;
+    const float var = group_sum(q, red + 16, nwaves) / (float)dim;
     rstd = (float)(1.0 / sqrt((double)var + (double)eps));
 }
 
-template <int NV, int FORM>
-__global__ __launch_bounds__(256) void k_adaln_fp8_wave(Fp8Args a)
+// Row index of a workgroup in the 2-D grid (x fastest); the grid can hold
+// more workgroups than rows.
+__device__ __forceinline__ int64_t grid_row() { return (int64_t)blockIdx.y * gridDim.x + blockIdx.x; }
+
+template <int VPT, int WAVES, int FORM>
+__global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.rows)
-        return;  // the whole wave leaves together
+    __shared__ float red[32];  // two sets of per-wave partials
+    constexpr int T = WAVES * 64;
+    const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;
-    const uint16_t* xr = a.x + row * dim;
-
-    uint4 xv[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-        xv[v] = ld16(xr, v * kWave + lane, nvec);
-
-    // Modulation operands, requested before the reductions.
-    const uint16_t* scr = nullptr;
-    const uint16_t* shr = nullptr;
-    if (FORM == kBcast) {
-        scr = a.scale;
-        shr = a.shift;
-    } else if (FORM == kPtok) {
-        scr = a.scale + row * dim;
-        shr = a.shift + row * dim;
-    } else if (FORM == kTable) {
-        scr = a.temb + (row * a.chunks + a.scale_idx) * dim;
-        shr = a.temb + (row * a.chunks + a.shift_idx) * dim;
-    }
-    uint4 scv[FORM == kNone ? 1 : NV], shv[FORM == kNone ? 1 : NV];
-    if (FORM != kNone) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            scv[v] = ld16(scr, v * kWave + lane, nvec);
-            shv[v] = ld16(shr, v * kWave + lane, nvec);
-        }
-    }
-
-    float mean, rstd;
-    row_stats<NV>(xv, lane, nvec, dim, a.eps, mean, rstd);
     const float inv = 1.0f / *a.act_scale;
+    const int64_t row = grid_row();
+    if (row >= a.rows)
+        return;  // whole workgroup
+    {
+        uint4 xv[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
+
+        // Modulation operands, requested before the reductions.  Per-token
+        // rows and temb chunks are streamed; broadcast vectors are shared by
+        // every row and kept in cache.
+        uint4 scv[FORM == kNone ? 1 : VPT], shv[FORM == kNone ? 1 : VPT];
+        if (FORM == kBcast) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                scv[v] = ld_row<false>(a.scale, v * T + t, nvec);
+                shv[v] = ld_row<false>(a.shift, v * T + t, nvec);
+            }
+        } else if (FORM == kPtok || FORM == kTable) {
+            const uint16_t* scr = FORM == kPtok ? a.scale + row * dim
+                                                : a.temb + (row * a.chunks + a.scale_idx) * dim;
+            const uint16_t* shr = FORM == kPtok ? a.shift + row * dim
+                                                : a.temb + (row * a.chunks + a.shift_idx) * dim;
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                scv[v] = ld_row<true>(scr, v * T + t, nvec);
+                shv[v] = ld_row<true>(shr, v * T + t, nvec);
+            }
+        }
+
+        float mean, rstd;
+        row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
 
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int i = v * kWave + lane;
-        if (i >= nvec)
-            continue;
-        float f[8], sc[8], sh[8];
-        unpack8(xv[v], f);
-        if (FORM == kNone) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sc[e] = 0.f;
-                sh[e] = 0.f;
-            }
-        } else {
-            unpack8(scv[v], sc);
-            unpack8(shv[v], sh);
-            if (FORM == kTable) {
-                float ts[8], th[8];
-                load_f32x8(a.table + (int64_t)a.scale_idx * dim + i * 8, ts);
-                load_f32x8(a.table + (int64_t)a.shift_idx * dim + i * 8, th);
+        for (int v = 0; v < VPT; ++v) {
+            const int i = v * T + t;
+            if (i >= nvec)
+                continue;
+            float f[8], sc[8], sh[8];
+            unpack8(xv[v], f);
+            if (FORM == kNone) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    sc[e] = sc[e] + ts[e];
-                    sh[e] = sh[e] + th[e];
+                    sc[e] = 0.f;
+                    sh[e] = 0.f;
+                }
+            } else {
+                unpack8(scv[v], sc);
+                unpack8(shv[v], sh);
+                if (FORM == kTable) {
+                    float ts[8], th[8];
+                    load_f32x8(a.table + (int64_t)a.scale_idx * dim + i * 8, ts);
+                    load_f32x8(a.table + (int64_t)a.shift_idx * dim + i * 8, th);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        sc[e] = sc[e] + ts[e];
+                        sh[e] = sh[e] + th[e];
+                    }
                 }
             }
-        }
-        float q[8];
+            float q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xhat = (f[e] - mean) * rstd;
-            const float y = (xhat * (1.0f + sc[e])) + sh[e];
-            q[e] = sat448(y * inv);
+            for (int e = 0; e < 8; ++e) {
+                const float xhat = (f[e] - mean) * rstd;
+                const float y = (xhat * (1.0f + sc[e])) + sh[e];
+                q[e] = sat448(y * inv);
+            }
+            st_stream(a.out + row * dim + (int64_t)i * 8,
+                      make_uint2(pack_e4m3x4(q[0], q[1], q[2], q[3]),
+                                 pack_e4m3x4(q[4], q[5], q[6], q[7])));
         }
-        uint2 o;
-        o.x = pack_e4m3x4(q[0], q[1], q[2], q[3]);
-        o.y = pack_e4m3x4(q[4], q[5], q[6], q[7]);
-        *reinterpret_cast<uint2*>(a.out + row * dim + (int64_t)i * 8) = o;
-    }
-    if (lane == 0) {
-        if (a.row_mean) a.row_mean[row] = mean;
-        if (a.row_rstd) a.row_rstd[row] = rstd;
+        if (t == 0) {
+            if (a.row_mean) a.row_mean[row] = mean;
+            if (a.row_rstd) a.row_rstd[row] = rstd;
+        }
     }
 }
 
-template <int NV>
-__global__ __launch_bounds__(256) void k_ln_fp4_wave(Fp4Args a)
+template <int VPT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.rows)
-        return;
+    __shared__ float red[32];  // two sets of per-wave partials
+    constexpr int T = WAVES * 64;
+    const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;  // even, since dim % 16 == 0
-    const uint16_t* xr = a.x + row * dim;
-
-    uint4 xv[NV];
+    const int64_t row = grid_row();
+    if (row >= a.rows)
+        return;  // whole workgroup
+    {
+        uint4 xv[VPT];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        xv[v] = ld16(xr, v * kWave + lane, nvec);
+        for (int v = 0; v < VPT; ++v)
+            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
 
-    float mean, rstd;
-    row_stats<NV>(xv, lane, nvec, dim, a.eps, mean, rstd);
+        float mean, rstd;
+        row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
 
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        // Both lanes of a block pair take the same branch: nvec is even.
-        const int i = v * kWave + lane;
-        if (i >= nvec)
-            continue;
-        float f[8], b[8];
-        unpack8(xv[v], f);
-        float amax = 0.f;
+        for (int v = 0; v < VPT; ++v) {
+            // The two halves of a 16-element block sit in lanes t and t ^ 1
+            // (T is a multiple of 64 and nvec is even, so both lanes of a
+            // pair take the same branch).
+            const int i = v * T + t;
+            if (i >= nvec)
+                continue;
+            float f[8], b[8];
+            unpack8(xv[v], f);
+            float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            // Normalize, then stage through bf16 (round to nearest even).
-            const uint32_t w = pack_bf16x2((f[e] - mean) * rstd, (f[e + 1] - mean) * rstd);
-            b[e] = bf16_lo(w);
-            b[e + 1] = bf16_hi(w);
-            amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
+            for (int e = 0; e < 8; e += 2) {
+                // Normalize, then stage through bf16 (round to nearest even).
+                const uint32_t w = pack_bf16x2((f[e] - mean) * rstd, (f[e + 1] - mean) * rstd);
+                b[e] = bf16_lo(w);
+                b[e + 1] = bf16_hi(w);
+                amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
+            }
+            amax = pair_max(amax);
+            const float target = fminf(amax / 6.0f, 448.0f);
+            const uint32_t scode = pack_e4m3x4(target, 0.f, 0.f, 0.f) & 0xFFu;
+            const float s = e4m3_value(scode);
+            uint32_t word = 0;
+            if (s != 0.f) {
+                const float enc = 1.0f / s;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    word |= e2m1_code(b[e] * enc) << (4 * e);
+            }
+            st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
+            if ((t & 1) == 0)
+                a.sf[row * (dim / 16) + (i >> 1)] = (uint8_t)scode;
         }
-        amax = pair_max(amax);
-        const float target = fminf(amax / 6.0f, 448.0f);
-        const uint32_t scode = pack_e4m3x4(target, 0.f, 0.f, 0.f) & 0xFFu;
-        const float s = e4m3_value(scode);
-        uint32_t word = 0;
-        if (s != 0.f) {
-            const float enc = 1.0f / s;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                word |= e2m1_code(b[e] * enc) << (4 * e);
+        if (t == 0) {
+            if (a.row_mean) a.row_mean[row] = mean;
+            if (a.row_rstd) a.row_rstd[row] = rstd;
         }
-        *reinterpret_cast<uint32_t*>(a.packed + row * (dim / 2) + (int64_t)i * 4) = word;
-        if ((lane & 1) == 0)
-            a.sf[row * (dim / 16) + (i >> 1)] = (uint8_t)scode;
-    }
-    if (lane == 0) {
-        if (a.row_mean) a.row_mean[row] = mean;
-        if (a.row_rstd) a.row_rstd[row] = rstd;
     }
 }
 
@@ -258,12 +280,12 @@ __device__ __forceinline__ void block_row_stats(const uint16_t* xr, int dim, flo
 __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
 {
     __shared__ float lds4[4];
-    const int64_t row = blockIdx.x;
     const int dim = a.dim;
+    const float inv = 1.0f / *a.act_scale;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const uint16_t* xr = a.x + row * dim;
     float mean, rstd;
     block_row_stats(xr, dim, a.eps, lds4, mean, rstd);
-    const float inv = 1.0f / *a.act_scale;
     for (int j = threadIdx.x; j < dim; j += 256) {
         float sc = 0.f, sh = 0.f;
         if (form == kBcast) {
@@ -286,14 +308,15 @@ __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
         if (a.row_mean) a.row_mean[row] = mean;
         if (a.row_rstd) a.row_rstd[row] = rstd;
     }
+    }
 }
 
 // One thread per 16-element block.
 __global__ __launch_bounds__(256) void k_ln_fp4_block(Fp4Args a)
 {
     __shared__ float lds4[4];
-    const int64_t row = blockIdx.x;
     const int dim = a.dim;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const uint16_t* xr = a.x + row * dim;
     float mean, rstd;
     block_row_stats(xr, dim, a.eps, lds4, mean, rstd);
@@ -323,6 +346,7 @@ __global__ __launch_bounds__(256) void k_ln_fp4_block(Fp4Args a)
         if (a.row_mean) a.row_mean[row] = mean;
         if (a.row_rstd) a.row_rstd[row] = rstd;
     }
+    }
 }
 
 // ---- standalone quantizer ---------------------------------------------------
@@ -339,55 +363,104 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* v, const float* 
 
 // ---- launchers ----------------------------------------------------------------
 
-template <int FORM>
-static hipError_t launch_fp8_wave(const Fp8Args& a, int nv, hipStream_t s)
+// Grid cap for the workgroup-per-row fallback, whose rows loop.
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+RowShape row_shape(int dim)
 {
-    const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
-    switch (nv) {
-#define ALNP_CASE(N) \
-    case N: hipLaunchKernelGGL((k_adaln_fp8_wave<N, FORM>), grid, block, 0, s, a); break;
-        ALNP_CASE(1) ALNP_CASE(2) ALNP_CASE(3) ALNP_CASE(4) ALNP_CASE(5) ALNP_CASE(6)
-        ALNP_CASE(7) ALNP_CASE(8) ALNP_CASE(9) ALNP_CASE(10) ALNP_CASE(11) ALNP_CASE(12)
-        ALNP_CASE(13) ALNP_CASE(14) ALNP_CASE(15) ALNP_CASE(16)
-#undef ALNP_CASE
-    default: return hipErrorInvalidValue;
+    // Waves per row (1, 2, 4 or 8) and 16-byte vectors per thread (1..8) for
+    // a row of dim/8 vectors: the least padding, with 2-4 vectors per thread
+    // preferred (fewer waves and barriers than 1, shorter per-wave tails than
+    // 5-8), then 3.
+    const int nvec = dim / 8;
+    RowShape best{0, 0};
+    double best_score = 1e30;
+    for (int vpt = 1; vpt <= 8; ++vpt) {
+        int waves = 1;
+        while (waves * 64 * vpt < nvec && waves < 8)
+            waves *= 2;
+        if (waves * 64 * vpt < nvec)
+            continue;
+        const double waste = double(waves * 64 * vpt - nvec) / nvec;
+        const double score = waste + (vpt == 1 ? 0.1 : vpt > 4 ? 0.02 * (vpt - 4) : 0.0) +
+                             (vpt == 3 ? -1e-3 : 0.0);
+        if (score < best_score) {
+            best_score = score;
+            best = RowShape{waves * 64, vpt};
+        }
     }
+    return best;
+}
+
+// One workgroup per row on a 2-D grid: x up to 65535 rows, y the rest.
+static dim3 row_grid(int64_t rows)
+{
+    const int64_t gx = std::min<int64_t>(rows, 65535);
+    return dim3((unsigned)gx, (unsigned)((rows + gx - 1) / gx));
+}
+
+#define ALNP_VPT_CASES(WAVES, LAUNCH)                                               \
+    switch (rs.vpt) {                                                               \
+    case 1: LAUNCH(1, WAVES); break;                                                \
+    case 2: LAUNCH(2, WAVES); break;                                                \
+    case 3: LAUNCH(3, WAVES); break;                                                \
+    case 4: LAUNCH(4, WAVES); break;                                                \
+    case 5: LAUNCH(5, WAVES); break;                                                \
+    case 6: LAUNCH(6, WAVES); break;                                                \
+    case 7: LAUNCH(7, WAVES); break;                                                \
+    case 8: LAUNCH(8, WAVES); break;                                                \
+    default: return hipErrorInvalidValue;                                           \
+    }
+
+#define ALNP_SHAPE_CASES(LAUNCH)                                                    \
+    switch (rs.threads) {                                                           \
+    case 64: ALNP_VPT_CASES(1, LAUNCH) break;                                       \
+    case 128: ALNP_VPT_CASES(2, LAUNCH) break;                                      \
+    case 256: ALNP_VPT_CASES(4, LAUNCH) break;                                      \
+    case 512: ALNP_VPT_CASES(8, LAUNCH) break;                                      \
+    default: return hipErrorInvalidValue;                                           \
+    }
+
+template <int FORM>
+static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid(a.rows);
+#define ALNP_LAUNCH(V, W) \
+    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM>), grid, dim3(W * 64), 0, s, a)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
     return hipGetLastError();
 }
 
 hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s)
 {
-    if (fast) {
-        const int nv = (a.dim / 8 + kWave - 1) / kWave;
+    const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0) {
         switch (form) {
-        case kNone: return launch_fp8_wave<kNone>(a, nv, s);
-        case kBcast: return launch_fp8_wave<kBcast>(a, nv, s);
-        case kPtok: return launch_fp8_wave<kPtok>(a, nv, s);
-        case kTable: return launch_fp8_wave<kTable>(a, nv, s);
+        case kNone: return launch_fp8_rows<kNone>(a, rs, s);
+        case kBcast: return launch_fp8_rows<kBcast>(a, rs, s);
+        case kPtok: return launch_fp8_rows<kPtok>(a, rs, s);
+        case kTable: return launch_fp8_rows<kTable>(a, rs, s);
         default: return hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(k_adaln_fp8_block, dim3((unsigned)a.rows), dim3(256), 0, s, a, form);
+    const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
+    hipLaunchKernelGGL(k_adaln_fp8_block, grid, dim3(256), 0, s, a, form);
     return hipGetLastError();
 }
 
 hipError_t launch_ln_fp4(const Fp4Args& a, bool fast, hipStream_t s)
 {
-    if (fast) {
-        const int nv = (a.dim / 8 + kWave - 1) / kWave;
-        const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
-        switch (nv) {
-#define ALNP_CASE(N) \
-    case N: hipLaunchKernelGGL((k_ln_fp4_wave<N>), grid, block, 0, s, a); break;
-            ALNP_CASE(1) ALNP_CASE(2) ALNP_CASE(3) ALNP_CASE(4) ALNP_CASE(5) ALNP_CASE(6)
-            ALNP_CASE(7) ALNP_CASE(8) ALNP_CASE(9) ALNP_CASE(10) ALNP_CASE(11) ALNP_CASE(12)
-            ALNP_CASE(13) ALNP_CASE(14) ALNP_CASE(15) ALNP_CASE(16)
-#undef ALNP_CASE
-        default: return hipErrorInvalidValue;
-        }
+    const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0) {
+        const dim3 grid = row_grid(a.rows);
+#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_ln_fp4_rows<V, W>), grid, dim3(W * 64), 0, s, a)
+        ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_ln_fp4_block, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
+    hipLaunchKernelGGL(k_ln_fp4_block, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

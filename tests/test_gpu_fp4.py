@@ -31,7 +31,8 @@ def check(got, ref, what):
 
 
 @pytest.mark.parametrize("rows,dim", [(1, 3072), (7, 16), (16, 2048), (65, 1536), (63, 1152),
-                                      (9, 5376), (3, 8192), (5, 48), (3, 8208), (2, 12016)])
+                                      (9, 5376), (3, 8192), (5, 48), (3, 8208), (2, 12016),
+                                      (2, 20480), (1, 32768), (2, 32784)])
 def test_small_shapes(orc, rows, dim):
     print(f"fp4 rows={rows} dim={dim}", flush=True)
     d = inputs.make("fp4", rows=rows, dim=dim, seed=rows + dim)

@@ -2,7 +2,7 @@
 oracle, through the C ABI: small and ragged shapes compared element by
 element, the full-size workloads on sampled rows, the edge cases (one row,
 tails of a partial wave, the workgroup-per-row fallback for dims that are
-not a multiple of 8 or above 8192 and for unaligned pointers), and the
+not a multiple of 8 or above 32768 and for unaligned pointers), and the
 identities between forms, batch invariance and determinism on the GPU."""
 import numpy as np
 import pytest
@@ -16,7 +16,9 @@ from parity import (act, assert_codes_close, assert_stats_close, dev_bf16, dev_f
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 2048), (7, 3072), (16, 2048), (63, 1536), (65, 1152), (257, 512), (5, 8),
-          (9, 5376), (3, 8192), (4, 2), (6, 6), (5, 1030), (3, 8200), (2, 12000)]
+          (9, 5376), (3, 8192), (4, 2), (6, 6), (5, 1030), (3, 8200), (2, 12000),
+          (3, 10240), (2, 16384), (2, 20480), (1, 24576), (1, 28672), (2, 32768),
+          (2, 32776), (1, 40000)]
 
 
 def run_gpu(kind, d, rows, dim, x=None, out=None):
