@@ -111,6 +111,20 @@ __device__ __forceinline__ uint32_t e2m1_code(float v)
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// Eight floats -> eight e2m1 codes packed low nibble first (element e in
+// bits 4e..4e+3), by v_cvt_scalef32_pk_fp4_f32 with scale 1: round to
+// nearest even onto the e2m1 grid, saturating at +-6, sign kept (matches
+// e2m1_code for every non-NaN input).
+__device__ __forceinline__ uint32_t pack_e2m1x8(float a, float b, float c, float d, float e,
+                                                float f, float g, float h)
+{
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c, d, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e, f, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, g, h, 1.0f, 3);
+    return w;
+}
+
 // ---- wave reductions ------------------------------------------------------
 
 template <int CTRL>

@@ -35,15 +35,6 @@ namespace alnp {
 
 enum Form { kNone = 0, kBcast = 1, kPtok = 2, kTable = 3 };
 
-// Eight consecutive fp32 of `p` starting at element e (16-byte aligned).
-__device__ __forceinline__ void load_f32x8(const float* p, float f[8])
-{
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
 // ---- fast path: one workgroup per row, row held in registers ---------------
 
 // Vector i of a row (eight elements), or zeros past the row end.
@@ -115,6 +106,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         // rows and temb chunks are streamed; broadcast vectors are shared by
         // every row and kept in cache.
         uint4 scv[FORM == kNone ? 1 : VPT], shv[FORM == kNone ? 1 : VPT];
+        // Table rows (fp32, shared by every row, L2-resident): also requested
+        // before the reductions so their latency is not added at the end.
+        float4 tsv[FORM == kTable ? 2 * VPT : 1], thv[FORM == kTable ? 2 * VPT : 1];
+        if (FORM == kTable) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const int i = v * T + t;
+                const int j = i < nvec ? 8 * i : 0;
+                const float4* ts = reinterpret_cast<const float4*>(a.table + (int64_t)a.scale_idx * dim + j);
+                const float4* th = reinterpret_cast<const float4*>(a.table + (int64_t)a.shift_idx * dim + j);
+                tsv[2 * v] = ts[0];
+                tsv[2 * v + 1] = ts[1];
+                thv[2 * v] = th[0];
+                thv[2 * v + 1] = th[1];
+            }
+        }
         if (FORM == kBcast) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
@@ -153,9 +160,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 unpack8(scv[v], sc);
                 unpack8(shv[v], sh);
                 if (FORM == kTable) {
-                    float ts[8], th[8];
-                    load_f32x8(a.table + (int64_t)a.scale_idx * dim + i * 8, ts);
-                    load_f32x8(a.table + (int64_t)a.shift_idx * dim + i * 8, th);
+                    const float ts[8] = {tsv[2 * v].x, tsv[2 * v].y, tsv[2 * v].z, tsv[2 * v].w,
+                                         tsv[2 * v + 1].x, tsv[2 * v + 1].y, tsv[2 * v + 1].z,
+                                         tsv[2 * v + 1].w};
+                    const float th[8] = {thv[2 * v].x, thv[2 * v].y, thv[2 * v].z, thv[2 * v].w,
+                                         thv[2 * v + 1].x, thv[2 * v + 1].y, thv[2 * v + 1].z,
+                                         thv[2 * v + 1].w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         sc[e] = sc[e] + ts[e];
@@ -184,7 +194,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 template <int VPT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
 {
-    __shared__ float red[32];  // two sets of per-wave partials
+    __shared__ float red[32];     // two sets of per-wave partials
+    __shared__ float inv_s[128];  // 1 / s for every e4m3 scale code s
     constexpr int T = WAVES * 64;
     const int t = threadIdx.x;
     const int dim = a.dim;
@@ -192,53 +203,60 @@ __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
     const int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
-    {
-        uint4 xv[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; ++v)
-            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
+    // The encode factor 1 / s is an IEEE division per scale code; tabulate it
+    // once per workgroup instead of once per block.
+    for (int c = t; c < 128; c += T)
+        inv_s[c] = (c == 0 || c == 127) ? 0.f : 1.0f / e4m3_value((uint32_t)c);
 
-        float mean, rstd;
-        row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
+    uint4 xv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
 
+    float mean, rstd;
+    row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
+    if (WAVES == 1)
+        __syncthreads();  // inv_s visible (row_stats has no barrier for one wave)
+
+    // Block scale s = e4m3(amax / 6): amax is a bf16 value, and for every
+    // finite bf16 amax the product amax * RN(1/6) rounds to the same e4m3
+    // code as the correctly rounded quotient (checked exhaustively on the
+    // host), so the kernel multiplies.
+    const float kSixth = 1.0f / 6.0f;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            // The two halves of a 16-element block sit in lanes t and t ^ 1
-            // (T is a multiple of 64 and nvec is even, so both lanes of a
-            // pair take the same branch).
-            const int i = v * T + t;
-            if (i >= nvec)
-                continue;
-            float f[8], b[8];
-            unpack8(xv[v], f);
-            float amax = 0.f;
+    for (int v = 0; v < VPT; ++v) {
+        // The two halves of a 16-element block sit in lanes t and t ^ 1
+        // (T is a multiple of 64 and nvec is even, so both lanes of a pair
+        // take the same branch).
+        const int i = v * T + t;
+        if (i >= nvec)
+            continue;
+        float f[8], b[8];
+        unpack8(xv[v], f);
+        float amax = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                // Normalize, then stage through bf16 (round to nearest even).
-                const uint32_t w = pack_bf16x2((f[e] - mean) * rstd, (f[e + 1] - mean) * rstd);
-                b[e] = bf16_lo(w);
-                b[e + 1] = bf16_hi(w);
-                amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
-            }
-            amax = pair_max(amax);
-            const float target = fminf(amax / 6.0f, 448.0f);
-            const uint32_t scode = pack_e4m3x4(target, 0.f, 0.f, 0.f) & 0xFFu;
-            const float s = e4m3_value(scode);
-            uint32_t word = 0;
-            if (s != 0.f) {
-                const float enc = 1.0f / s;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    word |= e2m1_code(b[e] * enc) << (4 * e);
-            }
-            st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
-            if ((t & 1) == 0)
-                a.sf[row * (dim / 16) + (i >> 1)] = (uint8_t)scode;
+        for (int e = 0; e < 8; e += 2) {
+            // Normalize, then stage through bf16 (round to nearest even).
+            const uint32_t w = pack_bf16x2((f[e] - mean) * rstd, (f[e + 1] - mean) * rstd);
+            b[e] = bf16_lo(w);
+            b[e + 1] = bf16_hi(w);
+            amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
         }
-        if (t == 0) {
-            if (a.row_mean) a.row_mean[row] = mean;
-            if (a.row_rstd) a.row_rstd[row] = rstd;
+        amax = pair_max(amax);
+        const uint32_t scode = pack_e4m3x4(fminf(amax * kSixth, 448.0f), 0.f, 0.f, 0.f) & 0xFFu;
+        uint32_t word = 0;
+        if (scode != 0) {
+            const float enc = inv_s[scode];
+            word = pack_e2m1x8(b[0] * enc, b[1] * enc, b[2] * enc, b[3] * enc,
+                               b[4] * enc, b[5] * enc, b[6] * enc, b[7] * enc);
         }
+        st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
+        if ((t & 1) == 0)
+            a.sf[row * (dim / 16) + (i >> 1)] = (uint8_t)scode;
+    }
+    if (t == 0) {
+        if (a.row_mean) a.row_mean[row] = mean;
+        if (a.row_rstd) a.row_rstd[row] = rstd;
     }
 }
 
