@@ -169,6 +169,22 @@ __device__ __forceinline__ float group_sum(float v, float* slot, int nwaves)
     return r;
 }
 
+// Sum over `nwaves` consecutive waves starting at wave `first` of the
+// workgroup (the waves that share one row), same bits in every thread of
+// those waves.  Every thread of the workgroup must call it (it holds a
+// barrier); `slot` is LDS with one float per wave of the workgroup.
+__device__ __forceinline__ float subgroup_sum(float v, float* slot, int first, int nwaves)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        slot[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = slot[first];
+    for (int k = 1; k < nwaves; ++k)
+        r += slot[first + k];
+    return r;
+}
+
 // Max of a lane and its xor-1 partner (the two lanes holding one 16-element
 // FP4 block).
 __device__ __forceinline__ float pair_max(float v)

@@ -191,6 +191,127 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
     }
 }
 
+// Table form with the two selected fp32 table rows staged in LDS and shared by
+// the two rows of a workgroup.  Holding the table in registers costs ~50
+// VGPRs per thread, which leaves room for only 2048 of the 2520 rows of the
+// Wan workload on the chip at once; from LDS the kernel keeps the per-token
+// kernel's register budget and reads each table element from L2 once per
+// two rows instead of once per row.  The table loads (L2 hits) are issued
+// before the row loads so that the LDS fill does not wait behind them.
+constexpr int kTableRows = 2;     // rows per workgroup
+constexpr int kTableMaxDim = 8192; // 2 table rows * 8192 * 4 B = 64 KiB of LDS
+
+template <int VPT, int WAVES>
+__global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
+{
+    extern __shared__ float4 tab[];   // [0, dim/4): scale row, [dim/4, dim/2): shift row
+    __shared__ float red[2][kTableRows * WAVES];
+    constexpr int T = WAVES * 64;      // threads per row
+    constexpr int NT = kTableRows * T; // threads per workgroup
+    const int tid = threadIdx.x;
+    const int rr = tid / T, t = tid % T;
+    const int dim = a.dim;
+    const int nvec = dim >> 3;
+    const int n4 = dim >> 2;
+    const float inv = 1.0f / *a.act_scale;
+    const int64_t row = grid_row() * kTableRows + rr;
+    const bool valid = row < a.rows;
+
+    // Table rows first: up to 8 float4 per thread in flight, the rest (only
+    // for dims above 4 * 2 * NT ... 8192) loaded after the row operands.
+    const float4* tsrc = reinterpret_cast<const float4*>(a.table + (int64_t)a.scale_idx * dim);
+    const float4* thsrc = reinterpret_cast<const float4*>(a.table + (int64_t)a.shift_idx * dim);
+    constexpr int kFirst = 8;
+    float4 tv[kFirst];
+#pragma unroll
+    for (int k = 0; k < kFirst; ++k) {
+        const int idx = tid + k * NT;  // over the 2 * n4 table vectors
+        tv[k] = idx < n4 ? tsrc[idx] : idx < 2 * n4 ? thsrc[idx - n4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    const int64_t lrow = valid ? row : 0;
+    const uint16_t* xr = a.x + lrow * dim;
+    const uint16_t* scr = a.temb + (lrow * a.chunks + a.scale_idx) * dim;
+    const uint16_t* shr = a.temb + (lrow * a.chunks + a.shift_idx) * dim;
+    uint4 xv[VPT], scv[VPT], shv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        xv[v] = ld_row<true>(xr, valid ? v * T + t : nvec, nvec);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        scv[v] = ld_row<true>(scr, valid ? v * T + t : nvec, nvec);
+        shv[v] = ld_row<true>(shr, valid ? v * T + t : nvec, nvec);
+    }
+
+#pragma unroll
+    for (int k = 0; k < kFirst; ++k) {
+        const int idx = tid + k * NT;
+        if (idx < 2 * n4)
+            tab[idx] = tv[k];
+    }
+    for (int idx = tid + kFirst * NT; idx < 2 * n4; idx += NT)
+        tab[idx] = idx < n4 ? tsrc[idx] : thsrc[idx - n4];
+
+    // Row statistics over the row's WAVES waves (the barriers also publish
+    // the LDS table).
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        float f[8];
+        unpack8(xv[v], f);
+        s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+    }
+    const float mean = subgroup_sum(s, red[0], rr * WAVES, WAVES) / (float)dim;
+    float q = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        if (v * T + t < nvec) {
+            float f[8];
+            unpack8(xv[v], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = f[e] - mean;
+                q = __builtin_fmaf(d, d, q);
+            }
+        }
+    }
+    const float var = subgroup_sum(q, red[1], rr * WAVES, WAVES) / (float)dim;
+    const float rstd = (float)(1.0 / sqrt((double)var + (double)a.eps));
+    if (!valid)
+        return;
+
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * T + t;
+        if (i >= nvec)
+            continue;
+        float f[8], sc[8], sh[8];
+        unpack8(xv[v], f);
+        unpack8(scv[v], sc);
+        unpack8(shv[v], sh);
+        const float4 s0 = tab[2 * i], s1 = tab[2 * i + 1];
+        const float4 h0 = tab[n4 + 2 * i], h1 = tab[n4 + 2 * i + 1];
+        const float ts[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float th[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        float q8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float scale = sc[e] + ts[e];
+            const float shift = sh[e] + th[e];
+            const float xhat = (f[e] - mean) * rstd;
+            const float y = (xhat * (1.0f + scale)) + shift;
+            q8[e] = sat448(y * inv);
+        }
+        st_stream(a.out + row * dim + (int64_t)i * 8,
+                  make_uint2(pack_e4m3x4(q8[0], q8[1], q8[2], q8[3]),
+                             pack_e4m3x4(q8[4], q8[5], q8[6], q8[7])));
+    }
+    if (t == 0) {
+        if (a.row_mean) a.row_mean[row] = mean;
+        if (a.row_rstd) a.row_rstd[row] = rstd;
+    }
+}
+
 template <int VPT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
 {
@@ -450,9 +571,22 @@ static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
     return hipGetLastError();
 }
 
+static hipError_t launch_fp8_table_lds(const Fp8Args& a, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid((a.rows + kTableRows - 1) / kTableRows);
+    const size_t lds = 2 * (size_t)a.dim * sizeof(float);
+#define ALNP_LAUNCH(V, W) \
+    hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W>), grid, dim3(kTableRows * W * 64), lds, s, a)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+    return hipGetLastError();
+}
+
 hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s)
 {
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256)
+        return launch_fp8_table_lds(a, rs, s);
     if (rs.vpt > 0) {
         switch (form) {
         case kNone: return launch_fp8_rows<kNone>(a, rs, s);
