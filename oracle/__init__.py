@@ -42,7 +42,14 @@ _SIGS = {
     "orc_fp4_pack": [_P, _I64, _P],
     "orc_ln_fp4": [_P, _F, _I64, _I64, _P, _P, _P, _P, _P],
     "orc_modulation6": [_P, _P, _I64, _I64, _P],
+    "orc_adaln_fp8_modfp8": [_P, _P, _P, _F, _F, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_awq_adaln_fp8": [_P, _P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
+    "orc_adaln_fp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
+    "orc_sf_swizzle": [_P, _I64, _I64, _P],
 }
+
+_RESTYPES = {"orc_sf_swizzled_size": ([_I64, _I64], _I64),
+             "orc_sf_swizzled_offset": ([_I64, _I64, _I64], _I64)}
 
 _lib = None
 
@@ -59,6 +66,10 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = None
+        for name, (args, res) in _RESTYPES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
         _lib = L
     return _lib
 
@@ -239,6 +250,44 @@ def adaln_fp8_f32ops(x, scale_f32, shift_f32, act_scale, eps=1e-5, want_y=False)
     return out, mean, rstd, y
 
 
+def adaln_fp8_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, act_scale, eps=1e-5,
+                     want_y=False, threads=1):
+    """Broadcast AdaLN -> FP8 with e4m3 (dim,) operands times fp32 scalars."""
+    x = _c(x, np.uint16)
+    sf = _c(scale_fp8, np.uint8)
+    hf = _c(shift_fp8, np.uint8)
+    rows, dim = x.shape
+    assert sf.shape == (dim,) and hf.shape == (dim,)
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_adaln_fp8_modfp8(_rowptr(x, r0, dim), _ptr(sf), _ptr(hf), scale_deq,
+                                   shift_deq, act_scale, eps, r1 - r0, dim,
+                                   _rowptr(out, r0, dim), _rowptr(mean, r0, 1),
+                                   _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
+def awq_adaln_fp8(x, scale, shift, inv_s, act_scale, eps=1e-5, want_y=False, threads=1):
+    """Broadcast AdaLN -> per-channel inv_s smoothing -> FP8."""
+    x = _c(x, np.uint16)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    inv_s = _c(inv_s, np.uint16)
+    rows, dim = x.shape
+    assert scale.shape == shift.shape == inv_s.shape == (dim,)
+    out, mean, rstd, y = _fp8_outputs(rows, dim, want_y)
+
+    def run(r0, r1):
+        lib().orc_awq_adaln_fp8(_rowptr(x, r0, dim), _ptr(scale), _ptr(shift), _ptr(inv_s),
+                                act_scale, eps, r1 - r0, dim, _rowptr(out, r0, dim),
+                                _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1),
+                                _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, mean, rstd, y
+
+
 # ---- FP4 producer ---------------------------------------------------------
 
 def fp4_block_quant(b):
@@ -279,6 +328,45 @@ def ln_fp4(x, eps=1e-5, want_b=False, threads=1):
                          _rowptr(b, r0, dim))
     _parallel(rows, threads, run)
     return packed, sf, mean, rstd, b
+
+
+def adaln_fp4(x, scale, shift, eps=1e-5, want_b=False, threads=1):
+    """Broadcast AdaLN -> bf16 stage -> e2m1 packed + e4m3 block scales
+    (row-major).  Returns (packed, sf, mean, rstd, b)."""
+    x = _c(x, np.uint16)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    rows, dim = x.shape
+    assert dim % 16 == 0 and scale.shape == shift.shape == (dim,)
+    packed = np.empty((rows, dim // 2), np.uint8)
+    sf = np.empty((rows, dim // 16), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    b = np.empty((rows, dim), np.float32) if want_b else None
+
+    def run(r0, r1):
+        lib().orc_adaln_fp4(_rowptr(x, r0, dim), _ptr(scale), _ptr(shift), eps, r1 - r0, dim,
+                            _rowptr(packed, r0, dim // 2), _rowptr(sf, r0, dim // 16),
+                            _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1), _rowptr(b, r0, dim))
+    _parallel(rows, threads, run)
+    return packed, sf, mean, rstd, b
+
+
+def sf_swizzled_size(rows, cols):
+    return int(lib().orc_sf_swizzled_size(rows, cols))
+
+
+def sf_swizzled_offset(r, c, cols):
+    return int(lib().orc_sf_swizzled_offset(r, c, cols))
+
+
+def sf_swizzle(sf_rowmajor):
+    """Row-major (rows, cols) e4m3 scales -> 128x4 tiled buffer (padding 0)."""
+    sf = _c(sf_rowmajor, np.uint8)
+    rows, cols = sf.shape
+    out = np.empty(sf_swizzled_size(rows, cols), np.uint8)
+    lib().orc_sf_swizzle(_ptr(sf), rows, cols, _ptr(out))
+    return out
 
 
 # ---- six-way modulation ---------------------------------------------------

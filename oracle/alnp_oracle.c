@@ -30,6 +30,18 @@
  *      output k.
  *  R8  NaN inputs to e2m1 are outside the contract; they encode as a zero
  *      magnitude with the sign kept.
+ *  R9  modfp8 (README "Available Functions", "Tensor Contract": e4m3 (dim,)
+ *      scale/shift with fp32 dequantization scalars): the operand is the e4m3
+ *      value times its dequantization scalar, one fp32 multiplication.
+ *  R10 AWQ (README: per-channel bf16 inv_s (dim,)): activation-aware smoothing
+ *      multiplies the modulated value by inv_s[j] before the static-scale
+ *      quantization: q = e4m3((y * inv_s[j]) * (1/act_scale)), each
+ *      multiplication rounded.
+ *  R11 AdaLN -> FP4: the FP8 path's fp32 modulation, then the LN -> FP4 bf16
+ *      stage and block quantization (the pages fix the staging only for the
+ *      LN entry; the plainest reading applies it to the modulated value).
+ *  R12 Swizzled scales: NVIDIA's documented 128x4 tiled layout for block
+ *      scale factors.  Parity unpinned: the pages give only its name.
  */
 #include "alnp_oracle.h"
 
@@ -347,6 +359,63 @@ void orc_adaln_fp8_table(const uint16_t* x, const uint16_t* temb,
              0, 0, temb, table, chunks, shift_idx, scale_idx);
 }
 
+/* modfp8 (R9): e4m3 broadcast operands times fp32 dequantization scalars. */
+void orc_adaln_fp8_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
+                          const uint8_t* shift_fp8, float scale_deq,
+                          float shift_deq, float act_scale, float eps,
+                          int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                          float* rstd, float* y)
+{
+    float* sc = (float*)malloc((size_t)dim * sizeof(float));
+    float* sh = (float*)malloc((size_t)dim * sizeof(float));
+    for (int64_t j = 0; j < dim; ++j) {
+        sc[j] = (float)orc_e4m3_decode(scale_fp8[j]) * scale_deq;
+        sh[j] = (float)orc_e4m3_decode(shift_fp8[j]) * shift_deq;
+    }
+    float inv = reciprocal(act_scale);
+    for (int64_t r = 0; r < rows; ++r) {
+        float mu, rs;
+        row_stats(x + r * dim, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        row_adaln_fp8(x + r * dim, sc, sh, dim, inv, mu, rs, out + r * dim,
+                      y ? y + r * dim : 0);
+    }
+    free(sc);
+    free(sh);
+}
+
+/* AWQ (R10): per-channel inv_s multiplication before the quantization. */
+void orc_awq_adaln_fp8(const uint16_t* x, const uint16_t* scale,
+                       const uint16_t* shift, const uint16_t* inv_s,
+                       float act_scale, float eps, int64_t rows, int64_t dim,
+                       uint8_t* out, float* mean, float* rstd, float* y)
+{
+    float inv = reciprocal(act_scale);
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        float mu, rs;
+        row_stats(xr, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        for (int64_t j = 0; j < dim; ++j) {
+            float centered = orc_bf16_to_f32(xr[j]) - mu;
+            float xhat = centered * rs;
+            float t = 1.0f + orc_bf16_to_f32(scale[j]);
+            float u = xhat * t;
+            float yj = u + orc_bf16_to_f32(shift[j]);
+            if (y)
+                y[r * dim + j] = yj;
+            float smoothed = yj * orc_bf16_to_f32(inv_s[j]);
+            out[r * dim + j] = orc_e4m3_encode_sat(smoothed * inv);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* FP4 producer (R6).                                                         */
 /* ------------------------------------------------------------------------ */
@@ -411,6 +480,75 @@ void orc_ln_fp4(const uint16_t* x, float eps, int64_t rows, int64_t dim,
     }
     free(staged);
     free(codes);
+}
+
+/* AdaLN -> FP4 (R11): fp32 modulation, then bf16 stage and block quant. */
+void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
+                   const uint16_t* shift, float eps, int64_t rows, int64_t dim,
+                   uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
+                   float* b)
+{
+    float* staged = (float*)malloc((size_t)dim * sizeof(float));
+    uint8_t* codes = (uint8_t*)malloc((size_t)dim);
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        float mu, rs;
+        row_stats(xr, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        for (int64_t j = 0; j < dim; ++j) {
+            float centered = orc_bf16_to_f32(xr[j]) - mu;
+            float xhat = centered * rs;
+            float t = 1.0f + orc_bf16_to_f32(scale[j]);
+            float u = xhat * t;
+            float yj = u + orc_bf16_to_f32(shift[j]);
+            staged[j] = orc_bf16_to_f32(orc_f32_to_bf16(yj));
+            if (b)
+                b[r * dim + j] = staged[j];
+        }
+        for (int64_t k = 0; k < dim / 16; ++k)
+            orc_fp4_block_quant(staged + 16 * k, codes + 16 * k,
+                                &sf[r * (dim / 16) + k]);
+        orc_fp4_pack(codes, dim, packed + r * (dim / 2));
+    }
+    free(staged);
+    free(codes);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 128x4 tiled block-scale layout (R12; parity unpinned).                     */
+/* The (rows, cols) scale matrix is cut into tiles of 128 rows x 4 columns,   */
+/* stored one after another (tile row-major: all column tiles of the first    */
+/* 128 rows, then the next 128 rows), 512 bytes each.  Inside a tile the      */
+/* byte for (r, c) sits at (r mod 32) * 16 + (r div 32) * 4 + c: the four     */
+/* 32-row groups are interleaved so that one 16-byte unit holds the four      */
+/* column scales of rows r, r + 32, r + 64 and r + 96.                        */
+/* ------------------------------------------------------------------------ */
+
+static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int64_t orc_sf_swizzled_size(int64_t rows, int64_t cols)
+{
+    return round_up(rows, 128) * round_up(cols, 4);
+}
+
+int64_t orc_sf_swizzled_offset(int64_t r, int64_t c, int64_t cols)
+{
+    int64_t col_tiles = round_up(cols, 4) / 4;
+    int64_t tile = (r / 128) * col_tiles + (c / 4);
+    int64_t rr = r % 128, cc = c % 4;
+    return tile * 512 + (rr % 32) * 16 + (rr / 32) * 4 + cc;
+}
+
+void orc_sf_swizzle(const uint8_t* sf_rowmajor, int64_t rows, int64_t cols,
+                    uint8_t* out)
+{
+    memset(out, 0, (size_t)orc_sf_swizzled_size(rows, cols));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[orc_sf_swizzled_offset(r, c, cols)] = sf_rowmajor[r * cols + c];
 }
 
 /* ------------------------------------------------------------------------ */

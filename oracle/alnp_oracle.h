@@ -78,6 +78,21 @@ void orc_adaln_fp8_f32ops(const uint16_t* x, const float* scale,
                           int64_t rows, int64_t dim, uint8_t* out, float* mean,
                           float* rstd, float* y);
 
+/* FP8 variants of the README's function list.
+ * modfp8: broadcast modulation stored as e4m3 (dim,) with fp32 dequantization
+ * scalars: scale_j = e4m3(scale_fp8[j]) * scale_deq, same for shift.
+ * awq: broadcast bf16 scale/shift plus a per-channel bf16 inv_s (dim,):
+ * q = e4m3((y * inv_s[j]) * (1/act_scale)). */
+void orc_adaln_fp8_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
+                          const uint8_t* shift_fp8, float scale_deq,
+                          float shift_deq, float act_scale, float eps,
+                          int64_t rows, int64_t dim, uint8_t* out, float* mean,
+                          float* rstd, float* y);
+void orc_awq_adaln_fp8(const uint16_t* x, const uint16_t* scale,
+                       const uint16_t* shift, const uint16_t* inv_s,
+                       float act_scale, float eps, int64_t rows, int64_t dim,
+                       uint8_t* out, float* mean, float* rstd, float* y);
+
 /* ---- FP4 producer ------------------------------------------------------ */
 /* One block of 16 values -> 16 e2m1 codes (4-bit, sign in bit 3) and one
  * e4m3 block-scale code. */
@@ -90,6 +105,26 @@ void orc_fp4_pack(const uint8_t* codes, int64_t n, uint8_t* packed);
 void orc_ln_fp4(const uint16_t* x, float eps, int64_t rows, int64_t dim,
                 uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
                 float* b);
+
+/* Broadcast AdaLN -> FP4: y = (xhat * (1 + scale)) + shift in fp32 as on the
+ * FP8 path, then the same bf16 stage and block quantization as orc_ln_fp4.
+ * b (nullable) receives the bf16-staged y as fp32. */
+void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
+                   const uint16_t* shift, float eps, int64_t rows, int64_t dim,
+                   uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
+                   float* b);
+
+/* 128x4 tiled ("swizzled") block-scale layout -- parity unpinned: the pages
+ * name the layout but do not define it; this is the tiled layout NVIDIA
+ * documents for block-scaled GEMM operands (see the function comment).
+ * cols = dim / 16 scale columns. */
+int64_t orc_sf_swizzled_size(int64_t rows, int64_t cols);
+int64_t orc_sf_swizzled_offset(int64_t r, int64_t c, int64_t cols);
+/* Scatter a row-major (rows, cols) scale matrix into the swizzled buffer;
+ * every byte the layout does not cover by a real scale (padding rows and
+ * columns) is set to 0. */
+void orc_sf_swizzle(const uint8_t* sf_rowmajor, int64_t rows, int64_t cols,
+                    uint8_t* out);
 
 /* ---- six-way modulation ------------------------------------------------ */
 /* params (tokens, 6, dim) fp32, mod (6, dim) fp32 -> out (6, tokens, dim)

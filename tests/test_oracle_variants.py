@@ -1,0 +1,158 @@
+"""Pins for the oracle's FP8 variants (modfp8, AWQ), AdaLN -> FP4 and the
+128x4 scale layout ("adaptive-layernorm-producers" README, "Available
+Functions" and "Tensor Contract": e4m3 (dim,) modulation with fp32
+dequantization scalars, per-channel bf16 inv_s, the AdaLN NVFP4 entry and
+its swizzled scale buffer sized by swizzled_sf_size)."""
+import numpy as np
+import torch
+
+from dit_adaptive_layernorm_amd import inputs
+
+
+def e4m3_bits(v):
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_vals(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def bf16(v):
+    return inputs.to_bf16_bits(np.asarray(v, np.float32))
+
+
+# ---- modfp8 -------------------------------------------------------------------
+
+def test_modfp8_unit_dequant_equals_broadcast(orc):
+    """e4m3 values have at most 4 significant bits, so they are exact in bf16:
+    with scale_deq = shift_deq = 1 modfp8 is the broadcast form fed the
+    decoded values, bit for bit."""
+    d = inputs.make("bcast", rows=12, dim=1024, seed=21)
+    sc8 = e4m3_bits(inputs.normal_f32((1024,), 0.3, 21, 9))
+    sh8 = e4m3_bits(inputs.normal_f32((1024,), 0.3, 21, 10))
+    a = orc.adaln_fp8_modfp8(d["x"], sc8, sh8, 1.0, 1.0, 0.025, want_y=True)
+    b = orc.adaln_fp8_bcast(d["x"], bf16(e4m3_vals(sc8)), bf16(e4m3_vals(sh8)), 0.025, want_y=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_modfp8_dequant_scalars_scale_operands(orc):
+    """Power-of-two dequantization scalars scale the operands exactly; the
+    scale scalar and the shift scalar act on their own operand only."""
+    d = inputs.make("bcast", rows=6, dim=512, seed=22)
+    sc8 = e4m3_bits(inputs.normal_f32((512,), 0.2, 22, 9))
+    sh8 = e4m3_bits(inputs.normal_f32((512,), 0.2, 22, 10))
+    a = orc.adaln_fp8_modfp8(d["x"], sc8, sh8, 0.5, 4.0, 0.025, want_y=True)
+    b = orc.adaln_fp8_bcast(d["x"], bf16(e4m3_vals(sc8) * 0.5), bf16(e4m3_vals(sh8) * 4.0), 0.025,
+                            want_y=True)
+    assert np.array_equal(a[3], b[3]) and np.array_equal(a[0], b[0])
+    # scale code -1 (0xB8) with deq 1 zeroes xhat: y = shift exactly.
+    minus1 = np.full(512, 0xB8, np.uint8)
+    _, _, _, y = orc.adaln_fp8_modfp8(d["x"], minus1, sh8, 1.0, 4.0, 0.025, want_y=True)
+    assert np.array_equal(y, np.broadcast_to(e4m3_vals(sh8) * np.float32(4.0), y.shape))
+
+
+# ---- AWQ ----------------------------------------------------------------------
+
+def test_awq_unit_inv_s_equals_broadcast(orc):
+    d = inputs.make("bcast", rows=9, dim=768, seed=23)
+    one = bf16(np.ones(768))
+    a = orc.awq_adaln_fp8(d["x"], d["scale"], d["shift"], one, 0.025, want_y=True)
+    b = orc.adaln_fp8_bcast(d["x"], d["scale"], d["shift"], 0.025, want_y=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_awq_inv_s_two_equals_half_act_scale(orc):
+    """inv_s = 2 doubles y exactly, which is the same as halving act_scale
+    (1/0.0125f = 2 * (1/0.025f) = 80 in fp32)."""
+    d = inputs.make("bcast", rows=9, dim=768, seed=24)
+    two = bf16(np.full(768, 2.0))
+    a = orc.awq_adaln_fp8(d["x"], d["scale"], d["shift"], two, 0.025)[0]
+    b = orc.adaln_fp8_bcast(d["x"], d["scale"], d["shift"], 0.0125)[0]
+    assert np.float32(1) / np.float32(0.0125) == np.float32(80)
+    assert np.array_equal(a, b)
+
+
+def test_awq_per_channel(orc):
+    """Each channel's code is e4m3(y * inv_s[j] * 40) (library conversion)."""
+    d = inputs.make("bcast", rows=5, dim=256, seed=25)
+    inv_s = bf16(np.abs(inputs.normal_f32((256,), 1.0, 25, 11)) + 0.25)
+    out, _, _, y = orc.awq_adaln_fp8(d["x"], d["scale"], d["shift"], inv_s, 0.025, want_y=True)
+    iv = (inv_s.astype(np.uint32) << 16).view(np.float32)
+    v = (y * iv[None, :]).astype(np.float32) * np.float32(40.0)
+    ok = np.abs(v) < 448
+    assert np.array_equal(out[ok], e4m3_bits(v[ok]))
+    assert np.all(out[~ok] & 0x7F == 0x7E)
+
+
+# ---- AdaLN -> FP4 ---------------------------------------------------------------
+
+def test_adaln_fp4_zero_modulation_equals_ln_fp4(orc):
+    d = inputs.make("fp4", rows=20, dim=512, seed=26)
+    z = np.zeros(512, np.uint16)
+    a = orc.adaln_fp4(d["x"], z, z, want_b=True)
+    b = orc.ln_fp4(d["x"], want_b=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_adaln_fp4_scale_minus_one_quantizes_shift(orc):
+    """scale = -1 makes y = shift exactly; the codes are the block quantizer
+    applied to the shift vector."""
+    rows, dim = 3, 256
+    x = inputs.normal_bf16((rows, dim), 1.0, 27, 1)
+    sh = inputs.normal_bf16((dim,), 2.0, 27, 3)
+    packed, sf, _, _, b = orc.adaln_fp4(x, bf16(np.full(dim, -1.0)), sh, want_b=True)
+    shf = (sh.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(b, np.broadcast_to(shf, b.shape))
+    codes, scales = orc.fp4_block_quant(shf)
+    for r in range(rows):
+        assert np.array_equal(packed[r], orc.fp4_pack(codes))
+        assert np.array_equal(sf[r], scales)
+
+
+def test_adaln_fp4_staging_is_bf16_of_fp8_path_y(orc):
+    d = inputs.make("bcast", rows=10, dim=512, seed=28)
+    _, _, _, _, b = orc.adaln_fp4(d["x"], d["scale"], d["shift"], want_b=True)
+    _, _, _, y = orc.adaln_fp8_bcast(d["x"], d["scale"], d["shift"], 1.0, want_y=True)
+    assert np.array_equal(b, torch.from_numpy(y).to(torch.bfloat16).float().numpy())
+
+
+# ---- swizzled scale layout (parity unpinned: properties only) ---------------------
+
+def test_swizzle_is_a_bijection_onto_the_padded_buffer(orc):
+    for rows, cols in ((128, 4), (256, 192), (300, 48), (1, 1), (4096, 192), (129, 5)):
+        size = orc.sf_swizzled_size(rows, cols)
+        pr, pc = -(-rows // 128) * 128, -(-cols // 4) * 4
+        assert size == pr * pc
+        offs = np.array([orc.sf_swizzled_offset(r, c, cols) for r in range(0, pr, max(1, pr // 97))
+                         for c in range(pc)])
+        assert offs.min() >= 0 and offs.max() < size
+        if pr * pc <= 40000:
+            full = np.array([orc.sf_swizzled_offset(r, c, cols) for r in range(pr) for c in range(pc)])
+            assert np.array_equal(np.sort(full), np.arange(size))
+
+
+def test_swizzle_tiles_are_contiguous(orc):
+    cols = 12
+    for tr in range(2):
+        for tc in range(3):
+            offs = [orc.sf_swizzled_offset(128 * tr + r, 4 * tc + c, cols)
+                    for r in range(128) for c in range(4)]
+            base = (tr * 3 + tc) * 512
+            assert sorted(offs) == list(range(base, base + 512))
+
+
+def test_swizzle_scatter_and_padding(orc):
+    rows, cols = 130, 6
+    sf = np.arange(rows * cols, dtype=np.uint32).astype(np.uint8).reshape(rows, cols) | 1
+    out = orc.sf_swizzle(sf)
+    assert out.size == 256 * 8
+    for r in (0, 31, 32, 127, 128, 129):
+        for c in range(cols):
+            assert out[orc.sf_swizzled_offset(r, c, cols)] == sf[r, c]
+    covered = {orc.sf_swizzled_offset(r, c, cols) for r in range(rows) for c in range(cols)}
+    pad = np.array([i for i in range(out.size) if i not in covered])
+    assert np.all(out[pad] == 0)
