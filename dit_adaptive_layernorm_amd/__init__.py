@@ -12,10 +12,10 @@ This module only checks tensors and marshals pointers: every step runs in
 the HIP kernels, on the current torch stream.  If libalnp.so is missing or
 cannot be loaded the functions raise; there is no CPU fallback.
 
-Difference from the README: the FP4 entry takes its block scales in plain
-row-major (rows, dim // 16) order rather than the 128x4 swizzled layout; the
-function is named without "swizzled" and the buffer size comes from
-sf_size(rows, dim).
+FP4 block scales come in two layouts: the README's *_swizzled_* functions
+write the 128x4 tiled layout (buffer size swizzled_sf_size(rows, dim)); the
+functions without "swizzled" write plain row-major (rows, dim // 16) scales
+(size sf_size(rows, dim)).
 """
 from __future__ import annotations
 
@@ -45,6 +45,15 @@ SIGNATURES = {
     "alnp_sf_size": ([_I64, _I64], _I64),
     "alnp_adaln_modulation6_bf16": ([_P, _P, _I64, _I64, _I64, ctypes.POINTER(_P), _P], _I),
     "alnp_quant_fp8_static_f32": ([_P, _P, _I64, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_fp8_modfp8_bf16": (
+        [_P, _P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_awq_ada_layer_norm_quant_fp8_bf16": (
+        [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
+    "alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16": ([_P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_nvfp4_bf16": ([_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16": (
+        [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_swizzled_sf_size": ([_I64, _I64], _I64),
 }
 
 STATUS = {0: "ALNP_OK", -1: "ALNP_ERR_NULL", -2: "ALNP_ERR_SHAPE", -3: "ALNP_ERR_DIM",
@@ -169,6 +178,43 @@ def ada_layer_norm_quant_fp8_ptok_table_bf16(x, temb, table, act_scale, shift_id
     return out
 
 
+def _scalar(t, name):
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold one fp32 value")
+    return _dev(t, name, torch.float32, t.shape)
+
+
+def ada_layer_norm_quant_fp8_modfp8_bf16(x, scale_fp8, shift_fp8, scale_deq, shift_deq,
+                                         act_scale, eps=1e-5, out=None, row_mean=None,
+                                         row_rstd=None):
+    """Broadcast AdaLN -> FP8 with e4m3 (dim,) scale/shift and fp32 device
+    dequantization scalars."""
+    rows, dim = _x(x)
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_fp8_modfp8_bf16",
+           lib().alnp_ada_layer_norm_quant_fp8_modfp8_bf16(
+               x.data_ptr(), _dev(scale_fp8, "scale_fp8", torch.float8_e4m3fn, (dim,)),
+               _dev(shift_fp8, "shift_fp8", torch.float8_e4m3fn, (dim,)),
+               _scalar(scale_deq, "scale_deq"), _scalar(shift_deq, "shift_deq"),
+               _act(act_scale), eps, rows, dim, out.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return out
+
+
+def awq_ada_layer_norm_quant_fp8_bf16(x, scale, shift, inv_s, act_scale, eps=1e-5, out=None,
+                                      row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> per-channel inv_s (dim,) bf16 -> FP8."""
+    rows, dim = _x(x)
+    out = _fp8_out(out, x)
+    _check("alnp_awq_ada_layer_norm_quant_fp8_bf16", lib().alnp_awq_ada_layer_norm_quant_fp8_bf16(
+        x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (dim,)),
+        _dev(shift, "shift", torch.bfloat16, (dim,)), _dev(inv_s, "inv_s", torch.bfloat16, (dim,)),
+        _act(act_scale), eps, rows, dim, out.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+        _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return out
+
+
 def layer_norm_no_affine_quant_fp8_static_bf16(x, act_scale, eps=1e-5, out=None,
                                                row_mean=None, row_rstd=None):
     """LayerNorm (no affine) -> FP8."""
@@ -215,6 +261,74 @@ def layer_norm_no_affine_quant_nvfp4_bf16(x, eps=1e-5, packed=None, sf=None,
     return packed, sf
 
 
+def swizzled_sf_size(rows: int, dim: int) -> int:
+    """Bytes of the 128x4 tiled block-scale buffer."""
+    n = lib().alnp_swizzled_sf_size(rows, dim)
+    if n < 0:
+        raise AlnpError("alnp_swizzled_sf_size", int(n))
+    return int(n)
+
+
+def _fp4_outputs(x, rows, dim, packed, sf, swizzled):
+    if dim % 16:
+        raise ValueError("dim must be a multiple of 16")
+    if packed is None:
+        packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=x.device)
+    n_sf = swizzled_sf_size(rows, dim) if swizzled else sf_size(rows, dim)
+    if sf is None:
+        sf = torch.empty((n_sf,) if swizzled else (rows, dim // 16), dtype=torch.uint8,
+                         device=x.device)
+    _dev(packed, "packed", torch.uint8, (rows, dim // 2))
+    if sf.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("sf must be uint8 or float8_e4m3fn")
+    _dev(sf, "sf", sf.dtype)
+    if sf.numel() != n_sf:
+        raise ValueError(f"sf must hold {n_sf} bytes, got {sf.numel()}")
+    return packed, sf
+
+
+def layer_norm_no_affine_quant_nvfp4_swizzled_bf16(x, eps=1e-5, packed=None, sf_swizzled=None,
+                                                   row_mean=None, row_rstd=None):
+    """LayerNorm (no affine) -> e2m1 packed + e4m3 block scales in the 128x4
+    tiled layout."""
+    rows, dim = _x(x)
+    packed, sf = _fp4_outputs(x, rows, dim, packed, sf_swizzled, True)
+    _check("alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16",
+           lib().alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16(
+               x.data_ptr(), eps, rows, dim, packed.data_ptr(), sf.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return packed, sf
+
+
+def ada_layer_norm_quant_nvfp4_bf16(x, scale, shift, eps=1e-5, packed=None, sf=None,
+                                    row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> e2m1 packed + row-major e4m3 block scales."""
+    rows, dim = _x(x)
+    packed, sf = _fp4_outputs(x, rows, dim, packed, sf, False)
+    _check("alnp_ada_layer_norm_quant_nvfp4_bf16", lib().alnp_ada_layer_norm_quant_nvfp4_bf16(
+        x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (dim,)),
+        _dev(shift, "shift", torch.bfloat16, (dim,)), eps, rows, dim, packed.data_ptr(),
+        sf.data_ptr(), _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+        _stream()))
+    return packed, sf
+
+
+def ada_layer_norm_quant_nvfp4_swizzled_bf16(x, scale, shift, eps=1e-5, packed=None,
+                                             sf_swizzled=None, row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> e2m1 packed + e4m3 block scales in the 128x4 tiled
+    layout."""
+    rows, dim = _x(x)
+    packed, sf = _fp4_outputs(x, rows, dim, packed, sf_swizzled, True)
+    _check("alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16",
+           lib().alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(
+               x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (dim,)),
+               _dev(shift, "shift", torch.bfloat16, (dim,)), eps, rows, dim, packed.data_ptr(),
+               sf.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+               _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return packed, sf
+
+
 # ---- six-way modulation --------------------------------------------------------
 
 def adaln_modulation6_bf16(adaln_params, layer_modulation, out=None):
@@ -250,7 +364,10 @@ def quant_fp8_static_f32(v, act_scale, out=None):
 
 __all__ = [
     "ada_layer_norm_quant_fp8_bf16", "ada_layer_norm_quant_fp8_ptok_bf16",
-    "ada_layer_norm_quant_fp8_ptok_table_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
-    "layer_norm_no_affine_quant_nvfp4_bf16", "sf_size", "adaln_modulation6_bf16",
-    "quant_fp8_static_f32", "lib", "AlnpError", "SIGNATURES",
+    "ada_layer_norm_quant_fp8_ptok_table_bf16", "ada_layer_norm_quant_fp8_modfp8_bf16",
+    "awq_ada_layer_norm_quant_fp8_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
+    "layer_norm_no_affine_quant_nvfp4_bf16", "layer_norm_no_affine_quant_nvfp4_swizzled_bf16",
+    "ada_layer_norm_quant_nvfp4_bf16", "ada_layer_norm_quant_nvfp4_swizzled_bf16",
+    "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "quant_fp8_static_f32",
+    "lib", "AlnpError", "SIGNATURES",
 ]

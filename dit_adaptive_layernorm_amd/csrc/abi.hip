@@ -13,6 +13,21 @@ using alnp::Fp4Args;
 using alnp::Fp8Args;
 using alnp::Mod6Args;
 
+Fp8Args fp8_args(const uint16_t* x, const float* act_scale, float eps, int64_t rows,
+                       int64_t dim, uint8_t* out, float* row_mean, float* row_rstd)
+{
+    Fp8Args a{};
+    a.x = x;
+    a.act_scale = act_scale;
+    a.eps = eps;
+    a.rows = rows;
+    a.dim = (int)dim;
+    a.out = out;
+    a.row_mean = row_mean;
+    a.row_rstd = row_rstd;
+    return a;
+}
+
 constexpr int64_t kMaxRows = (int64_t(1) << 24) - 1;
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxQuantN = int64_t(1) << 31;
@@ -42,19 +57,26 @@ int run_fp8(Fp8Args a, int form, void* stream)
 {
     if (!a.x || !a.act_scale || !a.out)
         return ALNP_ERR_NULL;
-    if ((form == 1 || form == 2) && (!a.scale || !a.shift))
+    if ((form == alnp::kBcast || form == alnp::kPtok || form == alnp::kAwq) &&
+        (!a.scale || !a.shift))
         return ALNP_ERR_NULL;
-    if (form == 3 && (!a.temb || !a.table))
+    if (form == alnp::kAwq && !a.inv_s)
+        return ALNP_ERR_NULL;
+    if (form == alnp::kTable && (!a.temb || !a.table))
+        return ALNP_ERR_NULL;
+    if (form == alnp::kModFp8 && (!a.scale_fp8 || !a.shift_fp8 || !a.scale_deq || !a.shift_deq))
         return ALNP_ERR_NULL;
     if (!aligned(a.x, 2) || !aligned(a.act_scale, 4) || !aligned(a.scale, 2) ||
         !aligned(a.shift, 2) || !aligned(a.temb, 2) || !aligned(a.table, 4) ||
+        !aligned(a.inv_s, 2) || !aligned(a.scale_deq, 4) || !aligned(a.shift_deq, 4) ||
         !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
         return ALNP_ERR_ALIGN;
     if (int st = check_eps(a.eps))
         return st;
     const bool fast = a.dim % 8 == 0 && a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) &&
                       aligned(a.scale, 16) && aligned(a.shift, 16) && aligned(a.temb, 16) &&
-                      aligned(a.table, 16) && aligned(a.out, 8);
+                      aligned(a.table, 16) && aligned(a.inv_s, 16) && aligned(a.scale_fp8, 8) &&
+                      aligned(a.shift_fp8, 8) && aligned(a.out, 8);
     return launch_status(alnp::launch_adaln_fp8(a, form, fast, as_stream(stream)));
 }
 
@@ -86,9 +108,10 @@ int alnp_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
 {
     if (int st = check_rows_dim(rows, dim, 2))
         return st > 0 ? ALNP_OK : st;
-    Fp8Args a{x, scale, shift, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
-              out, row_mean, row_rstd};
-    return run_fp8(a, 1, stream);
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    a.scale = scale;
+    a.shift = shift;
+    return run_fp8(a, alnp::kBcast, stream);
 }
 
 int alnp_ada_layer_norm_quant_fp8_ptok_bf16(const uint16_t* x, const uint16_t* scale,
@@ -98,9 +121,10 @@ int alnp_ada_layer_norm_quant_fp8_ptok_bf16(const uint16_t* x, const uint16_t* s
 {
     if (int st = check_rows_dim(rows, dim, 2))
         return st > 0 ? ALNP_OK : st;
-    Fp8Args a{x, scale, shift, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
-              out, row_mean, row_rstd};
-    return run_fp8(a, 2, stream);
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    a.scale = scale;
+    a.shift = shift;
+    return run_fp8(a, alnp::kPtok, stream);
 }
 
 int alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(const uint16_t* x, const uint16_t* temb,
@@ -116,9 +140,13 @@ int alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(const uint16_t* x, const uint1
         return ALNP_ERR_SHAPE;
     if (shift_idx < 0 || shift_idx >= chunks || scale_idx < 0 || scale_idx >= chunks)
         return ALNP_ERR_INDEX;
-    Fp8Args a{x, nullptr, nullptr, temb, table, chunks, shift_idx, scale_idx, act_scale, eps,
-              rows, (int)dim, out, row_mean, row_rstd};
-    return run_fp8(a, 3, stream);
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    a.temb = temb;
+    a.table = table;
+    a.chunks = chunks;
+    a.shift_idx = shift_idx;
+    a.scale_idx = scale_idx;
+    return run_fp8(a, alnp::kTable, stream);
 }
 
 int alnp_layer_norm_no_affine_quant_fp8_static_bf16(const uint16_t* x, const float* act_scale,
@@ -128,26 +156,104 @@ int alnp_layer_norm_no_affine_quant_fp8_static_bf16(const uint16_t* x, const flo
 {
     if (int st = check_rows_dim(rows, dim, 2))
         return st > 0 ? ALNP_OK : st;
-    Fp8Args a{x, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, act_scale, eps, rows, (int)dim,
-              out, row_mean, row_rstd};
-    return run_fp8(a, 0, stream);
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    return run_fp8(a, alnp::kNone, stream);
 }
+
+int alnp_ada_layer_norm_quant_fp8_modfp8_bf16(const uint16_t* x, const uint8_t* scale_fp8,
+                                              const uint8_t* shift_fp8, const float* scale_deq,
+                                              const float* shift_deq, const float* act_scale,
+                                              float eps, int64_t rows, int64_t dim, uint8_t* out,
+                                              float* row_mean, float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    a.scale_fp8 = scale_fp8;
+    a.shift_fp8 = shift_fp8;
+    a.scale_deq = scale_deq;
+    a.shift_deq = shift_deq;
+    return run_fp8(a, alnp::kModFp8, stream);
+}
+
+int alnp_awq_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                           const uint16_t* shift, const uint16_t* inv_s,
+                                           const float* act_scale, float eps, int64_t rows,
+                                           int64_t dim, uint8_t* out, float* row_mean,
+                                           float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 2))
+        return st > 0 ? ALNP_OK : st;
+    Fp8Args a = fp8_args(x, act_scale, eps, rows, dim, out, row_mean, row_rstd);
+    a.scale = scale;
+    a.shift = shift;
+    a.inv_s = inv_s;
+    return run_fp8(a, alnp::kAwq, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Common tail of the FP4 producers (scale/shift null for LayerNorm only).
+int run_fp4(const uint16_t* x, const uint16_t* scale, const uint16_t* shift, bool modulated,
+            float eps, int64_t rows, int64_t dim, uint8_t* packed, uint8_t* sf, int layout,
+            float* row_mean, float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 16))
+        return st > 0 ? ALNP_OK : st;
+    if (!x || !packed || !sf || (modulated && (!scale || !shift)))
+        return ALNP_ERR_NULL;
+    if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(row_mean, 4) ||
+        !aligned(row_rstd, 4))
+        return ALNP_ERR_ALIGN;
+    if (int st = check_eps(eps))
+        return st;
+    Fp4Args a{x, scale, shift, eps, rows, (int)dim, packed, sf, layout, row_mean, row_rstd};
+    const bool fast = dim <= alnp::kMaxFastDim && aligned(x, 16) && aligned(scale, 16) &&
+                      aligned(shift, 16) && aligned(packed, 4);
+    return launch_status(alnp::launch_fp4(a, fast, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
 
 int alnp_layer_norm_no_affine_quant_nvfp4_bf16(const uint16_t* x, float eps, int64_t rows,
                                                int64_t dim, uint8_t* packed, uint8_t* sf,
                                                float* row_mean, float* row_rstd, void* stream)
 {
-    if (int st = check_rows_dim(rows, dim, 16))
-        return st > 0 ? ALNP_OK : st;
-    if (!x || !packed || !sf)
-        return ALNP_ERR_NULL;
-    if (!aligned(x, 2) || !aligned(row_mean, 4) || !aligned(row_rstd, 4))
-        return ALNP_ERR_ALIGN;
-    if (int st = check_eps(eps))
-        return st;
-    Fp4Args a{x, eps, rows, (int)dim, packed, sf, row_mean, row_rstd};
-    const bool fast = dim <= alnp::kMaxFastDim && aligned(x, 16) && aligned(packed, 4);
-    return launch_status(alnp::launch_ln_fp4(a, fast, as_stream(stream)));
+    return run_fp4(x, nullptr, nullptr, false, eps, rows, dim, packed, sf, alnp::kSfRowMajor,
+                   row_mean, row_rstd, stream);
+}
+
+int alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16(const uint16_t* x, float eps,
+                                                        int64_t rows, int64_t dim,
+                                                        uint8_t* packed, uint8_t* sf_swizzled,
+                                                        float* row_mean, float* row_rstd,
+                                                        void* stream)
+{
+    return run_fp4(x, nullptr, nullptr, false, eps, rows, dim, packed, sf_swizzled,
+                   alnp::kSfSwizzled, row_mean, row_rstd, stream);
+}
+
+int alnp_ada_layer_norm_quant_nvfp4_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps, int64_t rows,
+                                         int64_t dim, uint8_t* packed, uint8_t* sf,
+                                         float* row_mean, float* row_rstd, void* stream)
+{
+    return run_fp4(x, scale, shift, true, eps, rows, dim, packed, sf, alnp::kSfRowMajor,
+                   row_mean, row_rstd, stream);
+}
+
+int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(const uint16_t* x, const uint16_t* scale,
+                                                  const uint16_t* shift, float eps,
+                                                  int64_t rows, int64_t dim, uint8_t* packed,
+                                                  uint8_t* sf_swizzled, float* row_mean,
+                                                  float* row_rstd, void* stream)
+{
+    return run_fp4(x, scale, shift, true, eps, rows, dim, packed, sf_swizzled,
+                   alnp::kSfSwizzled, row_mean, row_rstd, stream);
 }
 
 int64_t alnp_sf_size(int64_t rows, int64_t dim)
@@ -157,6 +263,15 @@ int64_t alnp_sf_size(int64_t rows, int64_t dim)
     if (dim % 16 != 0)
         return ALNP_ERR_DIM;
     return rows * (dim / 16);
+}
+
+int64_t alnp_swizzled_sf_size(int64_t rows, int64_t dim)
+{
+    if (rows < 0 || rows > kMaxRows || dim <= 0 || dim > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (dim % 16 != 0)
+        return ALNP_ERR_DIM;
+    return alnp::sf_swizzled_size(rows, dim / 16);
 }
 
 int alnp_adaln_modulation6_bf16(const float* params, const float* layer_mod, int64_t batch,

@@ -89,6 +89,18 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+// Eight e4m3 codes (bytes of v, byte 0 first) -> eight floats, exact
+// (v_cvt_pk_f32_fp8).
+__device__ __forceinline__ void unpack_e4m3x8(const uint2& v, float f[8])
+{
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+
 // Value of a non-negative e4m3 code below 0x7F: m * 2^-9 (subnormal) or
 // (8 + m) * 2^(e - 10).
 __device__ __forceinline__ float e4m3_value(uint32_t code)

@@ -6,17 +6,32 @@
 
 namespace alnp {
 
+// Operand forms of the FP8 producers.
+enum Form {
+    kNone = 0,    // LayerNorm only: scale = shift = 0
+    kBcast = 1,   // bf16 (dim,) scale / shift
+    kPtok = 2,    // bf16 (rows, dim) scale / shift
+    kTable = 3,   // bf16 temb (rows, chunks, dim) chunk + fp32 table (chunks, dim) row
+    kModFp8 = 4,  // e4m3 (dim,) scale / shift times fp32 dequantization scalars
+    kAwq = 5      // bf16 (dim,) scale / shift, then y * inv_s[j] (bf16 (dim,))
+};
+
 // Arguments of the FP8 producers.  Unused operand pointers are null.
 struct Fp8Args {
     const uint16_t* x;
-    const uint16_t* scale;   // broadcast (dim,) or per-token (rows, dim)
+    const uint16_t* scale;      // broadcast (dim,) or per-token (rows, dim)
     const uint16_t* shift;
-    const uint16_t* temb;    // table form: (rows, chunks, dim)
-    const float* table;      // table form: (chunks, dim)
+    const uint16_t* temb;       // table form: (rows, chunks, dim)
+    const float* table;         // table form: (chunks, dim)
     int64_t chunks;
     int64_t shift_idx;
     int64_t scale_idx;
-    const float* act_scale;  // device scalar
+    const uint8_t* scale_fp8;   // modfp8 form: e4m3 (dim,)
+    const uint8_t* shift_fp8;
+    const float* scale_deq;     // modfp8 form: device fp32 scalars
+    const float* shift_deq;
+    const uint16_t* inv_s;      // AWQ form: bf16 (dim,)
+    const float* act_scale;     // device scalar
     float eps;
     int64_t rows;
     int dim;
@@ -25,13 +40,22 @@ struct Fp8Args {
     float* row_rstd;
 };
 
+// Block-scale layouts of the FP4 producers.
+enum SfLayout {
+    kSfRowMajor = 0,  // (rows, dim/16)
+    kSfSwizzled = 1   // 128x4 tiles (see sf_swizzled_offset)
+};
+
 struct Fp4Args {
     const uint16_t* x;
+    const uint16_t* scale;   // broadcast (dim,) bf16, or null for LayerNorm only
+    const uint16_t* shift;
     float eps;
     int64_t rows;
     int dim;
     uint8_t* packed;
     uint8_t* sf;
+    int sf_layout;
     float* row_mean;
     float* row_rstd;
 };
@@ -56,11 +80,19 @@ struct RowShape {
 };
 RowShape row_shape(int dim);
 
-// form: 0 LayerNorm only, 1 broadcast, 2 per-token, 3 table.
+// Bytes of the 128x4 tiled block-scale buffer for (rows, cols = dim/16)
+// scales: both dimensions rounded up to the tile.
+inline int64_t sf_swizzled_size(int64_t rows, int64_t cols)
+{
+    return (rows + 127) / 128 * 128 * ((cols + 3) / 4 * 4);
+}
+
+// form: a Form.
 // fast: row kernel (dim % 8 == 0, dim <= kMaxFastDim, operands
 // 16-byte aligned); otherwise the workgroup-per-row kernel.
 hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s);
-hipError_t launch_ln_fp4(const Fp4Args& a, bool fast, hipStream_t s);
+// LayerNorm (a.scale null) or broadcast AdaLN -> FP4, row-major or tiled scales.
+hipError_t launch_fp4(const Fp4Args& a, bool fast, hipStream_t s);
 hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
 hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t* out,
                             hipStream_t s);

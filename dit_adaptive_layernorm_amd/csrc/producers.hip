@@ -31,10 +31,6 @@
 
 namespace alnp {
 
-// ---- operand forms --------------------------------------------------------
-
-enum Form { kNone = 0, kBcast = 1, kPtok = 2, kTable = 3 };
-
 // ---- fast path: one workgroup per row, row held in registers ---------------
 
 // Vector i of a row (eight elements), or zeros past the row end.
@@ -84,11 +80,25 @@ __device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], int nvec, int 
 // more workgroups than rows.
 __device__ __forceinline__ int64_t grid_row() { return (int64_t)blockIdx.y * gridDim.x + blockIdx.x; }
 
+// Eight e4m3 operand codes of vector i of a (dim,) byte vector, or zeros.
+__device__ __forceinline__ uint2 ld_fp8x8(const uint8_t* p, int i, int nvec)
+{
+    if (i >= nvec)
+        return make_uint2(0, 0);
+    return *reinterpret_cast<const uint2*>(p + 8 * i);
+}
+
 template <int VPT, int WAVES, int FORM>
 __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 {
     __shared__ float red[32];  // two sets of per-wave partials
     constexpr int T = WAVES * 64;
+    // Register arrays per operand kind (size 1 where the form has none).
+    constexpr bool kBf16Ops = FORM == kBcast || FORM == kPtok || FORM == kTable || FORM == kAwq;
+    constexpr int NB = kBf16Ops ? VPT : 1;
+    constexpr int NT = FORM == kTable ? 2 * VPT : 1;
+    constexpr int N8 = FORM == kModFp8 ? VPT : 1;
+    constexpr int NI = FORM == kAwq ? VPT : 1;
     const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;
@@ -103,12 +113,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
             xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
 
         // Modulation operands, requested before the reductions.  Per-token
-        // rows and temb chunks are streamed; broadcast vectors are shared by
+        // rows and temb chunks are streamed; (dim,) vectors are shared by
         // every row and kept in cache.
-        uint4 scv[FORM == kNone ? 1 : VPT], shv[FORM == kNone ? 1 : VPT];
+        uint4 scv[NB], shv[NB];
+        uint2 sc8[N8], sh8[N8];
+        uint4 isv[NI];
         // Table rows (fp32, shared by every row, L2-resident): also requested
         // before the reductions so their latency is not added at the end.
-        float4 tsv[FORM == kTable ? 2 * VPT : 1], thv[FORM == kTable ? 2 * VPT : 1];
+        float4 tsv[NT], thv[NT];
         if (FORM == kTable) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
@@ -122,11 +134,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 thv[2 * v + 1] = th[1];
             }
         }
-        if (FORM == kBcast) {
+        if (FORM == kBcast || FORM == kAwq) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
                 scv[v] = ld_row<false>(a.scale, v * T + t, nvec);
                 shv[v] = ld_row<false>(a.shift, v * T + t, nvec);
+                if (FORM == kAwq)
+                    isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec);
             }
         } else if (FORM == kPtok || FORM == kTable) {
             const uint16_t* scr = FORM == kPtok ? a.scale + row * dim
@@ -138,7 +152,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 scv[v] = ld_row<true>(scr, v * T + t, nvec);
                 shv[v] = ld_row<true>(shr, v * T + t, nvec);
             }
+        } else if (FORM == kModFp8) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec);
+                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec);
+            }
         }
+        const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
+        const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
 
         float mean, rstd;
         row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
@@ -155,6 +177,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 for (int e = 0; e < 8; ++e) {
                     sc[e] = 0.f;
                     sh[e] = 0.f;
+                }
+            } else if (FORM == kModFp8) {
+                // Dequantize: e4m3 value times its fp32 scalar, one rounding.
+                unpack_e4m3x8(sc8[v], sc);
+                unpack_e4m3x8(sh8[v], sh);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sc[e] = sc[e] * sdeq;
+                    sh[e] = sh[e] * hdeq;
                 }
             } else {
                 unpack8(scv[v], sc);
@@ -173,11 +204,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                     }
                 }
             }
+            float is[8];
+            if (FORM == kAwq)
+                unpack8(isv[v], is);
             float q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xhat = (f[e] - mean) * rstd;
-                const float y = (xhat * (1.0f + sc[e])) + sh[e];
+                float y = (xhat * (1.0f + sc[e])) + sh[e];
+                if (FORM == kAwq)
+                    y = y * is[e];  // per-channel smoothing before the static scale
                 q[e] = sat448(y * inv);
             }
             st_stream(a.out + row * dim + (int64_t)i * 8,
@@ -312,15 +348,45 @@ __global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds
     }
 }
 
-template <int VPT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
+// Byte offset of block scale (r, c) in the 128x4 tiled layout for `cols`
+// scales per row: tiles of 128 rows x 4 scales, 512 bytes each, laid out
+// tile-row-major; inside a tile, (r mod 32) selects a 16-byte unit, (r div 32)
+// mod 4 the 4-byte group in it, c mod 4 the byte.
+__device__ __forceinline__ int64_t sf_swizzled_offset(int64_t r, int c, int cols)
+{
+    const int col_tiles = (cols + 3) >> 2;
+    const int64_t tile = (r >> 7) * col_tiles + (c >> 2);
+    const int rr = (int)(r & 127);
+    return tile * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (c & 3);
+}
+
+// Store the block scale of (row, c); in the tiled layout the writer of a
+// row's last scale also zeroes the row's padding columns.
+template <bool SWZ>
+__device__ __forceinline__ void store_scale(uint8_t* sf, int64_t row, int c, int cols, uint8_t code)
+{
+    if (!SWZ) {
+        sf[row * cols + c] = code;
+        return;
+    }
+    sf[sf_swizzled_offset(row, c, cols)] = code;
+    if (c == cols - 1)
+        for (int p = cols; p < ((cols + 3) & ~3); ++p)
+            sf[sf_swizzled_offset(row, p, cols)] = 0;
+}
+
+// LayerNorm (MOD = false) or broadcast AdaLN (MOD = true) -> FP4.
+template <int VPT, int WAVES, bool MOD, bool SWZ>
+__global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
 {
     __shared__ float red[32];     // two sets of per-wave partials
     __shared__ float inv_s[128];  // 1 / s for every e4m3 scale code s
     constexpr int T = WAVES * 64;
+    constexpr int NM = MOD ? VPT : 1;
     const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;  // even, since dim % 16 == 0
+    const int cols = dim >> 4;
     const int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
@@ -333,6 +399,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
+    uint4 scv[NM], shv[NM];
+    if (MOD) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            scv[v] = ld_row<false>(a.scale, v * T + t, nvec);
+            shv[v] = ld_row<false>(a.shift, v * T + t, nvec);
+        }
+    }
 
     float mean, rstd;
     row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
@@ -352,13 +426,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
         const int i = v * T + t;
         if (i >= nvec)
             continue;
-        float f[8], b[8];
+        float f[8], b[8], y[8];
         unpack8(xv[v], f);
+        if (MOD) {
+            float sc[8], sh[8];
+            unpack8(scv[v], sc);
+            unpack8(shv[v], sh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xhat = (f[e] - mean) * rstd;
+                y[e] = (xhat * (1.0f + sc[e])) + sh[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                y[e] = (f[e] - mean) * rstd;
+        }
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            // Normalize, then stage through bf16 (round to nearest even).
-            const uint32_t w = pack_bf16x2((f[e] - mean) * rstd, (f[e + 1] - mean) * rstd);
+            // Stage through bf16 (round to nearest even).
+            const uint32_t w = pack_bf16x2(y[e], y[e + 1]);
             b[e] = bf16_lo(w);
             b[e + 1] = bf16_hi(w);
             amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
@@ -373,7 +461,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_ln_fp4_rows(Fp4Args a)
         }
         st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
         if ((t & 1) == 0)
-            a.sf[row * (dim / 16) + (i >> 1)] = (uint8_t)scode;
+            store_scale<SWZ>(a.sf, row, i >> 1, cols, (uint8_t)scode);
     }
     if (t == 0) {
         if (a.row_mean) a.row_mean[row] = mean;
@@ -438,9 +526,17 @@ __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
                  a.table[(int64_t)a.scale_idx * dim + j];
             sh = ldbf(a.temb, (row * a.chunks + a.shift_idx) * dim + j) +
                  a.table[(int64_t)a.shift_idx * dim + j];
+        } else if (form == kModFp8) {
+            sc = __builtin_amdgcn_cvt_f32_fp8((int)a.scale_fp8[j], 0) * *a.scale_deq;
+            sh = __builtin_amdgcn_cvt_f32_fp8((int)a.shift_fp8[j], 0) * *a.shift_deq;
+        } else if (form == kAwq) {
+            sc = ldbf(a.scale, j);
+            sh = ldbf(a.shift, j);
         }
         const float xhat = (ldbf(xr, j) - mean) * rstd;
-        const float y = (xhat * (1.0f + sc)) + sh;
+        float y = (xhat * (1.0f + sc)) + sh;
+        if (form == kAwq)
+            y = y * ldbf(a.inv_s, j);
         a.out[row * dim + j] = (uint8_t)(pack_e4m3x4(sat448(y * inv), 0.f, 0.f, 0.f) & 0xFFu);
     }
     if (threadIdx.x == 0) {
@@ -450,8 +546,17 @@ __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
     }
 }
 
-// One thread per 16-element block.
-__global__ __launch_bounds__(256) void k_ln_fp4_block(Fp4Args a)
+// One thread per 16-element block; modulation when a.scale is non-null.
+__device__ __forceinline__ float fp4_block_y(const Fp4Args& a, const uint16_t* xr, int j,
+                                             float mean, float rstd)
+{
+    const float xhat = (ldbf(xr, j) - mean) * rstd;
+    if (!a.scale)
+        return xhat;
+    return (xhat * (1.0f + ldbf(a.scale, j))) + ldbf(a.shift, j);
+}
+
+__global__ __launch_bounds__(256) void k_fp4_block(Fp4Args a)
 {
     __shared__ float lds4[4];
     const int dim = a.dim;
@@ -464,7 +569,8 @@ __global__ __launch_bounds__(256) void k_ln_fp4_block(Fp4Args a)
         float amax = 0.f;
         for (int e = 0; e < 16; e += 2) {
             const int j = 16 * k + e;
-            const uint32_t w = pack_bf16x2((ldbf(xr, j) - mean) * rstd, (ldbf(xr, j + 1) - mean) * rstd);
+            const uint32_t w = pack_bf16x2(fp4_block_y(a, xr, j, mean, rstd),
+                                           fp4_block_y(a, xr, j + 1, mean, rstd));
             b[e] = bf16_lo(w);
             b[e + 1] = bf16_hi(w);
             amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
@@ -479,7 +585,10 @@ __global__ __launch_bounds__(256) void k_ln_fp4_block(Fp4Args a)
                 byte = e2m1_code(b[e] * enc) | (e2m1_code(b[e + 1] * enc) << 4);
             a.packed[row * (dim / 2) + 8 * k + e / 2] = (uint8_t)byte;
         }
-        a.sf[row * (dim / 16) + k] = (uint8_t)scode;
+        if (a.sf_layout == kSfSwizzled)
+            store_scale<true>(a.sf, row, k, dim / 16, (uint8_t)scode);
+        else
+            store_scale<false>(a.sf, row, k, dim / 16, (uint8_t)scode);
     }
     if (threadIdx.x == 0) {
         if (a.row_mean) a.row_mean[row] = mean;
@@ -593,6 +702,8 @@ hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s
         case kBcast: return launch_fp8_rows<kBcast>(a, rs, s);
         case kPtok: return launch_fp8_rows<kPtok>(a, rs, s);
         case kTable: return launch_fp8_rows<kTable>(a, rs, s);
+        case kModFp8: return launch_fp8_rows<kModFp8>(a, rs, s);
+        case kAwq: return launch_fp8_rows<kAwq>(a, rs, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -601,18 +712,27 @@ hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_ln_fp4(const Fp4Args& a, bool fast, hipStream_t s)
+template <bool MOD, bool SWZ>
+static hipError_t launch_fp4_rows(const Fp4Args& a, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid(a.rows);
+#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_fp4_rows<V, W, MOD, SWZ>), grid, dim3(W * 64), 0, s, a)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_fp4(const Fp4Args& a, bool fast, hipStream_t s)
 {
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
     if (rs.vpt > 0) {
-        const dim3 grid = row_grid(a.rows);
-#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_ln_fp4_rows<V, W>), grid, dim3(W * 64), 0, s, a)
-        ALNP_SHAPE_CASES(ALNP_LAUNCH)
-#undef ALNP_LAUNCH
-        return hipGetLastError();
+        const bool mod = a.scale != nullptr, swz = a.sf_layout == kSfSwizzled;
+        if (mod)
+            return swz ? launch_fp4_rows<true, true>(a, rs, s) : launch_fp4_rows<true, false>(a, rs, s);
+        return swz ? launch_fp4_rows<false, true>(a, rs, s) : launch_fp4_rows<false, false>(a, rs, s);
     }
     const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
-    hipLaunchKernelGGL(k_ln_fp4_block, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_fp4_block, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -134,6 +134,37 @@ int alnp_layer_norm_no_affine_quant_fp8_static_bf16(
     int64_t dim, uint8_t* out, float* row_mean, float* row_rstd, void* stream);
 
 /*
+ * Broadcast AdaLN -> FP8 with modulation stored as e4m3 (README:
+ * ada_layer_norm_quant_fp8_modfp8_bf16; "Tensor Contract": scale_fp8,
+ * shift_fp8 e4m3 (dim,); scale_deq, shift_deq device fp32 scalars).
+ *   scale[j] = e4m3(scale_fp8[j]) * (*scale_deq), one fp32 multiplication;
+ *   shift likewise; then the same normalize / modulate / quantize as above.
+ * dim must be even.
+ */
+int alnp_ada_layer_norm_quant_fp8_modfp8_bf16(const uint16_t* x,
+                                              const uint8_t* scale_fp8,
+                                              const uint8_t* shift_fp8,
+                                              const float* scale_deq,
+                                              const float* shift_deq,
+                                              const float* act_scale, float eps,
+                                              int64_t rows, int64_t dim,
+                                              uint8_t* out, float* row_mean,
+                                              float* row_rstd, void* stream);
+
+/*
+ * Broadcast AdaLN -> per-channel AWQ smoothing -> FP8 (README:
+ * awq_ada_layer_norm_quant_fp8_bf16; "Tensor Contract": inv_s bf16 (dim,)).
+ *   q = e4m3((y * inv_s[j]) * (1 / act_scale)), each multiplication rounded.
+ * dim must be even.
+ */
+int alnp_awq_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                           const uint16_t* shift, const uint16_t* inv_s,
+                                           const float* act_scale, float eps,
+                                           int64_t rows, int64_t dim, uint8_t* out,
+                                           float* row_mean, float* row_rstd,
+                                           void* stream);
+
+/*
  * LayerNorm (no affine) -> FP4 (README:
  * layer_norm_no_affine_quant_nvfp4_swizzled_bf16, with the block scales in
  * plain row-major order instead of the 128x4 swizzle).
@@ -156,6 +187,48 @@ int alnp_layer_norm_no_affine_quant_nvfp4_bf16(const uint16_t* x, float eps,
 /* Bytes of the row-major block-scale buffer for an FP4 output: rows*dim/16.
  * Returns a negative status for invalid sizes. */
 int64_t alnp_sf_size(int64_t rows, int64_t dim);
+
+/*
+ * LayerNorm (no affine) -> FP4 with the block scales in the 128x4 tiled
+ * ("swizzled") layout (README: layer_norm_no_affine_quant_nvfp4_swizzled_bf16;
+ * "Tensor Contract": "128x4 swizzled uint8 scale layout", allocate with
+ * swizzled_sf_size).  The pages name the layout without defining it; this is
+ * the tiled layout NVIDIA documents for block-scaled GEMM operands:
+ *   cols = dim / 16 scales per row; tiles of 128 rows x 4 scales, 512 bytes
+ *   each, stored tile-row-major; scale (r, c) lives at
+ *     ((r / 128) * ceil(cols / 4) + c / 4) * 512
+ *       + (r % 32) * 16 + ((r % 128) / 32) * 4 + (c % 4).
+ *   sf_swizzled holds alnp_swizzled_sf_size(rows, dim) bytes.  Padding
+ *   columns (cols rounded up to 4) of every written row are set to 0; padding
+ *   rows (rows rounded up to 128) are not written.
+ * packed, numerics and errors as for the row-major entry.
+ */
+int alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16(
+    const uint16_t* x, float eps, int64_t rows, int64_t dim, uint8_t* packed,
+    uint8_t* sf_swizzled, float* row_mean, float* row_rstd, void* stream);
+
+/*
+ * Broadcast AdaLN -> FP4 (README: ada_layer_norm_quant_nvfp4_swizzled_bf16,
+ * here with row-major scales; the _swizzled entry below takes the tiled
+ * layout).  scale, shift (dim,) bf16.  Per row: y = (xhat * (1 + scale)) +
+ * shift in fp32 exactly as on the FP8 path, then y is rounded to bf16 and
+ * quantized in blocks of 16 as for the LayerNorm entry.
+ */
+int alnp_ada_layer_norm_quant_nvfp4_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps,
+                                         int64_t rows, int64_t dim,
+                                         uint8_t* packed, uint8_t* sf,
+                                         float* row_mean, float* row_rstd,
+                                         void* stream);
+int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(
+    const uint16_t* x, const uint16_t* scale, const uint16_t* shift, float eps,
+    int64_t rows, int64_t dim, uint8_t* packed, uint8_t* sf_swizzled,
+    float* row_mean, float* row_rstd, void* stream);
+
+/* Bytes of the tiled block-scale buffer (README: swizzled_sf_size):
+ * ceil(rows / 128) * 128 * ceil(dim / 64) * 4.  Negative status for invalid
+ * sizes. */
+int64_t alnp_swizzled_sf_size(int64_t rows, int64_t dim);
 
 /*
  * Six-way DiT modulation (README: adaln_modulation6_bf16; "Tensor Contract":

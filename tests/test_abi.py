@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 10
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -100,6 +100,29 @@ def test_fp4_validation(L):
     assert L.alnp_sf_size(4096, 3000) == DIM
     assert L.alnp_sf_size(-1, 3072) == SHAPE
     assert alnp.sf_size(2, 32) == 4
+
+
+def test_variant_validation(L):
+    m = L.alnp_ada_layer_norm_quant_fp8_modfp8_bf16
+    assert m(A, B, C, None, D, D, 1e-5, 4, 64, A, None, None, None) == NULL
+    assert m(A, B, C, D, D + 2, D, 1e-5, 4, 64, A, None, None, None) == ALIGN
+    assert m(A, B, C, D, D, D, 1e-5, 4, 63, A, None, None, None) == DIM
+    assert m(None, None, None, None, None, None, 1e-5, 0, 64, None, None, None, None) == OK
+    w = L.alnp_awq_ada_layer_norm_quant_fp8_bf16
+    assert w(A, B, C, None, D, 1e-5, 4, 64, A, None, None, None) == NULL
+    assert w(A, B, C, D + 1, D, 1e-5, 4, 64, A, None, None, None) == ALIGN
+    f = L.alnp_ada_layer_norm_quant_nvfp4_bf16
+    assert f(A, None, C, 1e-5, 4, 64, B, C, None, None, None) == NULL
+    assert f(A, B, C, 1e-5, 4, 40, B, C, None, None, None) == DIM
+    g = L.alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16
+    assert g(A, B, C + 2 - 1, 1e-5, 4, 64, B, C, None, None, None) == ALIGN
+    h = L.alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16
+    assert h(A, 1e-5, 4, 64, B, None, None, None, None) == NULL
+    assert L.alnp_swizzled_sf_size(4096, 3072) == 4096 * 192
+    assert L.alnp_swizzled_sf_size(130, 48) == 256 * 4
+    assert L.alnp_swizzled_sf_size(1, 16) == 128 * 4
+    assert L.alnp_swizzled_sf_size(5, 24) == DIM
+    assert alnp.swizzled_sf_size(300, 3072) == 384 * 192
 
 
 def test_modulation6_validation(L):

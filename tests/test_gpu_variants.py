@@ -1,0 +1,218 @@
+"""Parity of the FP8 variants (modfp8, AWQ) and the FP4 variants (AdaLN->FP4,
+128x4 tiled scales) with the oracle, through the C ABI: small and ragged
+shapes (fast and fallback kernels), a full Wan-size shape on sampled rows,
+every finite e4m3 operand code, and the tiled layout's padding rules."""
+import numpy as np
+import pytest
+import torch
+
+import dit_adaptive_layernorm_amd as alnp
+from dit_adaptive_layernorm_amd import inputs
+from parity import (act, assert_codes_close, assert_stats_close, dev_bf16, e2m1_ordinal,
+                    e4m3_ordinal, host_u8, misaligned_like, sample_rows, unpack_e2m1)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 2048), (7, 3072), (63, 1536), (65, 1152), (9, 5376), (3, 8192), (5, 8),
+          (4, 2), (5, 1030), (2, 12000), (2, 32768), (1, 40000)]
+FP4_SHAPES = [(1, 3072), (7, 16), (65, 1536), (63, 1152), (9, 5376), (3, 8192), (5, 48),
+              (3, 8208), (2, 20480), (2, 32784), (130, 3072), (129, 80)]
+
+
+def e4m3_codes(f32):
+    return torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def dev_u8_as_fp8(u8):
+    return torch.from_numpy(np.ascontiguousarray(u8)).cuda().view(torch.float8_e4m3fn)
+
+
+def scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+# ---- modfp8 -------------------------------------------------------------------
+
+def modfp8_inputs(rows, dim, seed):
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=seed)
+    d["scale_fp8"] = e4m3_codes(inputs.normal_f32((dim,), 0.3, seed, 9))
+    d["shift_fp8"] = e4m3_codes(inputs.normal_f32((dim,), 0.3, seed, 10))
+    return d
+
+
+def run_modfp8(d, sdeq, hdeq, x=None):
+    rows, dim = d["x"].shape
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    o = alnp.ada_layer_norm_quant_fp8_modfp8_bf16(
+        dev_bf16(d["x"]) if x is None else x, dev_u8_as_fp8(d["scale_fp8"]),
+        dev_u8_as_fp8(d["shift_fp8"]), scalar(sdeq), scalar(hdeq), act(0.025),
+        row_mean=mean, row_rstd=rstd)
+    return host_u8(o), mean.cpu().numpy(), rstd.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,dim", SHAPES)
+def test_modfp8_shapes(orc, rows, dim):
+    print(f"modfp8 rows={rows} dim={dim}", flush=True)
+    d = modfp8_inputs(rows, dim, rows + dim)
+    got, m, r = run_modfp8(d, 0.75, 1.5)
+    ref, rm, rr, _ = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5, 0.025)
+    assert_codes_close(got, ref, e4m3_ordinal, f"modfp8 {rows}x{dim}")
+    assert_stats_close(m, r, rm, rr)
+
+
+def test_modfp8_every_finite_operand_code(orc):
+    dim = 2048
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    d = inputs.make("bcast", rows=16, dim=dim, seed=31)
+    d["scale_fp8"] = np.resize(codes, dim).astype(np.uint8)
+    d["shift_fp8"] = np.resize(codes[::-1], dim).astype(np.uint8)
+    for sdeq, hdeq in ((1.0, 1.0), (0.01, 0.37), (2.0, 0.5)):
+        got, _, _ = run_modfp8(d, sdeq, hdeq)
+        ref = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], sdeq, hdeq, 0.025)[0]
+        assert_codes_close(got, ref, e4m3_ordinal, f"modfp8 codes deq {sdeq}/{hdeq}")
+
+
+def test_modfp8_full_size_sampled(orc):
+    d = modfp8_inputs(2520, 3072, 32)
+    got, m, r = run_modfp8(d, 1.0, 1.0)
+    sel = sample_rows(2520, 128)
+    ref, rm, rr, _ = orc.adaln_fp8_modfp8(np.ascontiguousarray(d["x"][sel]), d["scale_fp8"],
+                                          d["shift_fp8"], 1.0, 1.0, 0.025, threads=8)
+    assert_codes_close(got[sel], ref, e4m3_ordinal, "modfp8 2520x3072")
+    assert_stats_close(m[sel], r[sel], rm, rr)
+
+
+def test_modfp8_unaligned_fallback(orc):
+    d = modfp8_inputs(9, 3072, 33)
+    x = misaligned_like((9, 3072), torch.bfloat16)
+    x.copy_(dev_bf16(d["x"]))
+    got, _, _ = run_modfp8(d, 0.5, 2.0, x=x)
+    ref = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.5, 2.0, 0.025)[0]
+    assert_codes_close(got, ref, e4m3_ordinal, "modfp8 unaligned")
+
+
+# ---- AWQ --------------------------------------------------------------------------
+
+def awq_inputs(rows, dim, seed):
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=seed)
+    d["inv_s"] = inputs.to_bf16_bits(np.abs(inputs.normal_f32((dim,), 0.5, seed, 11)) + 0.5)
+    return d
+
+
+def run_awq(d, x=None):
+    rows, dim = d["x"].shape
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    o = alnp.awq_ada_layer_norm_quant_fp8_bf16(
+        dev_bf16(d["x"]) if x is None else x, dev_bf16(d["scale"]), dev_bf16(d["shift"]),
+        dev_bf16(d["inv_s"]), act(0.025), row_mean=mean, row_rstd=rstd)
+    return host_u8(o), mean.cpu().numpy(), rstd.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,dim", SHAPES)
+def test_awq_shapes(orc, rows, dim):
+    print(f"awq rows={rows} dim={dim}", flush=True)
+    d = awq_inputs(rows, dim, 3 * rows + dim)
+    got, m, r = run_awq(d)
+    ref, rm, rr, _ = orc.awq_adaln_fp8(d["x"], d["scale"], d["shift"], d["inv_s"], 0.025)
+    assert_codes_close(got, ref, e4m3_ordinal, f"awq {rows}x{dim}")
+    assert_stats_close(m, r, rm, rr)
+
+
+def test_awq_unit_inv_s_equals_broadcast_bitwise():
+    d = inputs.make("bcast", rows=300, dim=3072, seed=34)
+    x, s, h = dev_bf16(d["x"]), dev_bf16(d["scale"]), dev_bf16(d["shift"])
+    one = torch.ones(3072, dtype=torch.bfloat16, device="cuda")
+    a = host_u8(alnp.awq_ada_layer_norm_quant_fp8_bf16(x, s, h, one, act()))
+    b = host_u8(alnp.ada_layer_norm_quant_fp8_bf16(x, s, h, act()))
+    assert np.array_equal(a, b)
+
+
+# ---- AdaLN -> FP4 and tiled scales ---------------------------------------------------
+
+def fp4_check(got_packed, got_sf, ref_packed, ref_sf, what):
+    assert_codes_close(unpack_e2m1(got_packed), unpack_e2m1(ref_packed), e2m1_ordinal, what + " codes")
+    assert_codes_close(got_sf, ref_sf, e4m3_ordinal, what + " scales")
+
+
+def swizzled_positions(orc, rows, cols):
+    return np.array([[orc.sf_swizzled_offset(r, c, cols) for c in range(cols)]
+                     for r in range(rows)], np.int64)
+
+
+@pytest.mark.parametrize("rows,dim", FP4_SHAPES)
+def test_adaln_fp4_rowmajor_shapes(orc, rows, dim):
+    print(f"adaln fp4 rows={rows} dim={dim}", flush=True)
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=rows + 5 * dim)
+    packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(dev_bf16(d["x"]), dev_bf16(d["scale"]),
+                                                      dev_bf16(d["shift"]))
+    rp, rs, _, _, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"])
+    fp4_check(host_u8(packed), host_u8(sf), rp, rs, f"adaln fp4 {rows}x{dim}")
+
+
+@pytest.mark.parametrize("mod", [False, True])
+@pytest.mark.parametrize("rows,dim", [(1, 3072), (130, 3072), (129, 80), (7, 48), (2, 32784),
+                                      (300, 1536)])
+def test_fp4_swizzled_layout(orc, mod, rows, dim):
+    print(f"fp4 swizzled mod={mod} rows={rows} dim={dim}", flush=True)
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=7 * rows + dim)
+    cols = dim // 16
+    size = alnp.swizzled_sf_size(rows, dim)
+    sentinel = 0xA5
+    sf = torch.full((size,), sentinel, dtype=torch.uint8, device="cuda")
+    x = dev_bf16(d["x"])
+    if mod:
+        packed, sf = alnp.ada_layer_norm_quant_nvfp4_swizzled_bf16(
+            x, dev_bf16(d["scale"]), dev_bf16(d["shift"]), sf_swizzled=sf)
+        rp, rs, _, _, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"])
+    else:
+        packed, sf = alnp.layer_norm_no_affine_quant_nvfp4_swizzled_bf16(x, sf_swizzled=sf)
+        rp, rs, _, _, _ = orc.ln_fp4(d["x"])
+    got = host_u8(sf)
+    pos = swizzled_positions(orc, rows, cols)
+    fp4_check(host_u8(packed), got[pos], rp, rs, f"swizzled {rows}x{dim}")
+    # Padding columns of written rows are zero; padding rows are untouched.
+    pc = -(-cols // 4) * 4
+    for r in range(rows):
+        for c in range(cols, pc):
+            assert got[orc.sf_swizzled_offset(r, c, cols)] == 0
+    pr = -(-rows // 128) * 128
+    for r in range(rows, pr):
+        for c in range(pc):
+            assert got[orc.sf_swizzled_offset(r, c, cols)] == sentinel
+    # The same scales as the row-major entry, moved.
+    if mod:
+        _, sf_rm = alnp.ada_layer_norm_quant_nvfp4_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]))
+    else:
+        _, sf_rm = alnp.layer_norm_no_affine_quant_nvfp4_bf16(x)
+    assert np.array_equal(got[pos], host_u8(sf_rm))
+
+
+def test_adaln_fp4_zero_modulation_equals_ln_fp4_bitwise():
+    d = inputs.make("fp4", rows=512, dim=3072, seed=35)
+    x = dev_bf16(d["x"])
+    z = torch.zeros(3072, dtype=torch.bfloat16, device="cuda")
+    p1, s1 = alnp.ada_layer_norm_quant_nvfp4_bf16(x, z, z)
+    p2, s2 = alnp.layer_norm_no_affine_quant_nvfp4_bf16(x)
+    assert np.array_equal(host_u8(p1), host_u8(p2)) and np.array_equal(host_u8(s1), host_u8(s2))
+
+
+def test_adaln_fp4_full_size_sampled(orc):
+    d = inputs.make("bcast", rows=4096, dim=3072, seed=36)
+    packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(dev_bf16(d["x"]), dev_bf16(d["scale"]),
+                                                      dev_bf16(d["shift"]))
+    sel = sample_rows(4096, 128)
+    rp, rs, _, _, _ = orc.adaln_fp4(np.ascontiguousarray(d["x"][sel]), d["scale"], d["shift"],
+                                    threads=8)
+    fp4_check(host_u8(packed)[sel], host_u8(sf)[sel], rp, rs, "adaln fp4 4096x3072")
+
+
+def test_adaln_fp4_unaligned_fallback(orc):
+    d = inputs.make("bcast", rows=11, dim=3072, seed=37)
+    x = misaligned_like((11, 3072), torch.bfloat16)
+    x.copy_(dev_bf16(d["x"]))
+    packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]))
+    rp, rs, _, _, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"])
+    fp4_check(host_u8(packed), host_u8(sf), rp, rs, "adaln fp4 unaligned")
