@@ -54,6 +54,7 @@ SIGNATURES = {
     "alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16": (
         [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_swizzled_sf_size": ([_I64, _I64], _I64),
+    "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
 
 STATUS = {0: "ALNP_OK", -1: "ALNP_ERR_NULL", -2: "ALNP_ERR_SHAPE", -3: "ALNP_ERR_DIM",
@@ -349,6 +350,32 @@ def adaln_modulation6_bf16(adaln_params, layer_modulation, out=None):
     return tuple(out)
 
 
+# ---- residual gate ---------------------------------------------------------------
+
+def gated_residual_bf16(residual, gate, proj, out=None):
+    """out = bf16(residual + bf16(gate * proj)); gate (rows, dim) or (dim,).
+    Pass out=residual to update the residual stream in place."""
+    if residual.dim() != 2:
+        raise ValueError("residual must be 2-D (rows, dim)")
+    rows, dim = residual.shape
+    _dev(residual, "residual", torch.bfloat16)
+    _dev(proj, "proj", torch.bfloat16, (rows, dim))
+    if tuple(gate.shape) == (dim,):
+        gate_rows = 1
+    elif tuple(gate.shape) == (rows, dim):
+        gate_rows = rows
+    else:
+        raise ValueError(f"gate must be ({dim},) or ({rows}, {dim})")
+    _dev(gate, "gate", torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(residual)
+    _dev(out, "out", torch.bfloat16, (rows, dim))
+    _check("alnp_gated_residual_bf16", lib().alnp_gated_residual_bf16(
+        residual.data_ptr(), gate.data_ptr(), proj.data_ptr(), rows, dim, gate_rows,
+        out.data_ptr(), _stream()))
+    return out
+
+
 # ---- standalone quantizer --------------------------------------------------------
 
 def quant_fp8_static_f32(v, act_scale, out=None):
@@ -368,6 +395,7 @@ __all__ = [
     "awq_ada_layer_norm_quant_fp8_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
     "layer_norm_no_affine_quant_nvfp4_bf16", "layer_norm_no_affine_quant_nvfp4_swizzled_bf16",
     "ada_layer_norm_quant_nvfp4_bf16", "ada_layer_norm_quant_nvfp4_swizzled_bf16",
-    "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "quant_fp8_static_f32",
+    "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "gated_residual_bf16",
+    "quant_fp8_static_f32",
     "lib", "AlnpError", "SIGNATURES",
 ]

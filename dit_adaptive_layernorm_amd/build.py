@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libalnp.so")
-SOURCES = ["producers.hip", "modulation6.hip", "abi.hip"]
+SOURCES = ["producers.hip", "modulation6.hip", "residual.hip", "abi.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

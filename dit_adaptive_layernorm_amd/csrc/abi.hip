@@ -301,6 +301,25 @@ int alnp_adaln_modulation6_bf16(const float* params, const float* layer_mod, int
     return launch_status(alnp::launch_modulation6(a, fast, as_stream(stream)));
 }
 
+int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
+                             const uint16_t* proj, int64_t rows, int64_t dim, int64_t gate_rows,
+                             uint16_t* out, void* stream)
+{
+    if (rows < 0 || rows > kMaxRows || dim <= 0 || dim > kMaxDim ||
+        (gate_rows != 1 && gate_rows != rows))
+        return ALNP_ERR_SHAPE;
+    if (rows == 0)
+        return ALNP_OK;
+    if (!residual || !gate || !proj || !out)
+        return ALNP_ERR_NULL;
+    if (!aligned(residual, 2) || !aligned(gate, 2) || !aligned(proj, 2) || !aligned(out, 2))
+        return ALNP_ERR_ALIGN;
+    alnp::GateArgs a{residual, gate, proj, rows, (int)dim, gate_rows, out};
+    const bool fast = dim % 8 == 0 && aligned(residual, 16) && aligned(gate, 16) &&
+                      aligned(proj, 16) && aligned(out, 16);
+    return launch_status(alnp::launch_gated_residual(a, fast, as_stream(stream)));
+}
+
 int alnp_quant_fp8_static_f32(const float* v, const float* act_scale, int64_t n, uint8_t* out,
                               void* stream)
 {

@@ -68,6 +68,16 @@ struct Mod6Args {
     uint16_t* out[6];
 };
 
+struct GateArgs {
+    const uint16_t* residual;  // (rows, dim)
+    const uint16_t* gate;      // (gate_rows, dim), gate_rows 1 or rows
+    const uint16_t* proj;      // (rows, dim)
+    int64_t rows;
+    int dim;
+    int64_t gate_rows;
+    uint16_t* out;             // (rows, dim), may be residual
+};
+
 // Largest row (elements) the register-resident row kernels take: 8 waves,
 // 8 vectors of 8 elements per thread.
 constexpr int kMaxFastDim = 8 * 64 * 8 * 8;
@@ -94,6 +104,8 @@ hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s
 // LayerNorm (a.scale null) or broadcast AdaLN -> FP4, row-major or tiled scales.
 hipError_t launch_fp4(const Fp4Args& a, bool fast, hipStream_t s);
 hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
+// fast: dim % 8 == 0 and every pointer 16-byte aligned.
+hipError_t launch_gated_residual(const GateArgs& a, bool fast, hipStream_t s);
 hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t* out,
                             hipStream_t s);
 

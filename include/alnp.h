@@ -245,6 +245,23 @@ int alnp_adaln_modulation6_bf16(const float* params, const float* layer_mod,
                                 uint16_t* const out[6], void* stream);
 
 /*
+ * Residual gate step (the residual-gate epilogue whose numerical program the
+ * h3-blackwell-runtime page fixes: bf16 projection output, gate
+ * multiplication with its bf16 boundary, bf16 residual added, final bf16
+ * rounding).  The gate is a six-way producer output chunk (per token) or a
+ * (dim,) vector:
+ *   out[r, j] = bf16_rne(residual[r, j] + bf16_rne(gate[g, j] * proj[r, j]))
+ * with g = r when gate_rows == rows and g = 0 when gate_rows == 1.
+ *   residual, proj, out  (rows, dim) bf16; out may be residual itself
+ *                        (in-place x += gate * proj); no other overlap.
+ *   gate                 (gate_rows, dim) bf16, gate_rows 1 or rows.
+ * Other gate_rows values return ALNP_ERR_SHAPE.
+ */
+int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
+                             const uint16_t* proj, int64_t rows, int64_t dim,
+                             int64_t gate_rows, uint16_t* out, void* stream);
+
+/*
  * Static-scale FP8 quantizer on its own, the last stage of every FP8
  * producer: out[i] = e4m3(v[i] * (1 / act_scale)), same rounding and
  * saturation as above.  n >= 0 elements of fp32 input.

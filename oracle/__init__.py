@@ -46,6 +46,7 @@ _SIGS = {
     "orc_awq_adaln_fp8": [_P, _P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
     "orc_adaln_fp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
     "orc_sf_swizzle": [_P, _I64, _I64, _P],
+    "orc_gated_residual": [_P, _P, _P, _I64, _I64, _I64, _P],
 }
 
 _RESTYPES = {"orc_sf_swizzled_size": ([_I64, _I64], _I64),
@@ -366,6 +367,22 @@ def sf_swizzle(sf_rowmajor):
     rows, cols = sf.shape
     out = np.empty(sf_swizzled_size(rows, cols), np.uint8)
     lib().orc_sf_swizzle(_ptr(sf), rows, cols, _ptr(out))
+    return out
+
+
+# ---- residual gate ----------------------------------------------------------
+
+def gated_residual(residual, gate, proj):
+    """bf16(residual + bf16(gate * proj)); gate (dim,) or (rows, dim)."""
+    res = _c(residual, np.uint16)
+    g = _c(gate, np.uint16)
+    pr = _c(proj, np.uint16)
+    rows, dim = res.shape
+    assert pr.shape == (rows, dim)
+    gate_rows = 1 if g.shape == (dim,) else rows
+    assert g.size == gate_rows * dim
+    out = np.empty((rows, dim), np.uint16)
+    lib().orc_gated_residual(_ptr(res), _ptr(g), _ptr(pr), rows, dim, gate_rows, _ptr(out))
     return out
 
 

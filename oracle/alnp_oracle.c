@@ -42,6 +42,10 @@
  *      LN entry; the plainest reading applies it to the modulated value).
  *  R12 Swizzled scales: NVIDIA's documented 128x4 tiled layout for block
  *      scale factors.  Parity unpinned: the pages give only its name.
+ *  R13 Residual gate (h3 page, the residual-gate epilogue's numerical
+ *      program: bf16 GEMM output, gate multiplication with its bf16
+ *      boundary, bf16 residual added, final bf16 rounding):
+ *      out = bf16(residual + bf16(gate * proj)), fp32 arithmetic.
  */
 #include "alnp_oracle.h"
 
@@ -549,6 +553,25 @@ void orc_sf_swizzle(const uint8_t* sf_rowmajor, int64_t rows, int64_t cols,
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c)
             out[orc_sf_swizzled_offset(r, c, cols)] = sf_rowmajor[r * cols + c];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Residual gate (R13).                                                       */
+/* ------------------------------------------------------------------------ */
+
+void orc_gated_residual(const uint16_t* residual, const uint16_t* gate,
+                        const uint16_t* proj, int64_t rows, int64_t dim,
+                        int64_t gate_rows, uint16_t* out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* g = gate + (gate_rows == 1 ? 0 : r * dim);
+        for (int64_t j = 0; j < dim; ++j) {
+            float gated = orc_bf16_to_f32(g[j]) * orc_bf16_to_f32(proj[r * dim + j]);
+            float gated_bf16 = orc_bf16_to_f32(orc_f32_to_bf16(gated));
+            float sum = orc_bf16_to_f32(residual[r * dim + j]) + gated_bf16;
+            out[r * dim + j] = orc_f32_to_bf16(sum);
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -126,6 +126,14 @@ int64_t orc_sf_swizzled_offset(int64_t r, int64_t c, int64_t cols);
 void orc_sf_swizzle(const uint8_t* sf_rowmajor, int64_t rows, int64_t cols,
                     uint8_t* out);
 
+/* ---- residual gate ----------------------------------------------------- */
+/* out = bf16(residual + bf16(gate * proj)), elementwise over (rows, dim);
+ * gate is (gate_rows, dim) with gate_rows 1 (broadcast) or rows (per token).
+ * out may be residual itself. */
+void orc_gated_residual(const uint16_t* residual, const uint16_t* gate,
+                        const uint16_t* proj, int64_t rows, int64_t dim,
+                        int64_t gate_rows, uint16_t* out);
+
 /* ---- six-way modulation ------------------------------------------------ */
 /* params (tokens, 6, dim) fp32, mod (6, dim) fp32 -> out (6, tokens, dim)
  * bf16 planes; plane k holds chunk k. */

@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -138,6 +138,16 @@ def test_modulation6_validation(L):
     assert f(A, B, 1, 5, 64, P6(A, B, C, D + 1, A, B), None) == ALIGN
     assert f(A + 2, B, 1, 5, 64, outs, None) == ALIGN
     assert f(None, None, 0, 5, 64, None, None) == OK
+
+
+def test_gated_residual_validation(L):
+    f = L.alnp_gated_residual_bf16
+    assert f(A, B, C, 4, 64, 2, D, None) == SHAPE
+    assert f(A, B, C, -1, 64, 1, D, None) == SHAPE
+    assert f(A, B, C, 4, 0, 1, D, None) == SHAPE
+    assert f(A, None, C, 4, 64, 4, D, None) == NULL
+    assert f(A, B, C, 4, 64, 1, D + 1, None) == ALIGN
+    assert f(None, None, None, 0, 64, 0, None, None) == OK
 
 
 def test_quant_validation(L):
