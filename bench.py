@@ -54,6 +54,8 @@ def parse():
                    help="cold (rotating >= 512 MB of buffer sets), warm (one set), or both")
     p.add_argument("--direct", action="store_true",
                    help="launch each step directly instead of replaying a HIP graph")
+    p.add_argument("--no-overhead", action="store_true",
+                   help="skip the small-shape launch-overhead table")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run four plain device copies of 256 MiB (reference for "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -193,6 +195,92 @@ def time_producer(prod, steps, warmup, use_graph, torch, stream):
     return t0.elapsed_time(t1) * 1000.0 / steps
 
 
+# ---- launch overhead at small shapes ---------------------------------------------------
+
+def launch_overhead(torch, alnp, inputs, stream, calls=400, graph_launches=32, replays=50):
+    """The pages' small-shape method (Benchmark Results, "Six-way modulation
+    producer" and "NVIDIA Thor installed artifact"): per shape, the raw C ABI
+    launched directly, the Python wrapper launched directly (A-B-B-A order),
+    and a HIP graph of 32 launches replayed, time / 32.  Inputs stay the same
+    buffers (warm): these shapes are latency-bound."""
+    dev = torch.device("cuda")
+    bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    L = alnp.lib()
+    cases = {}
+    act = torch.tensor([0.025], dtype=torch.float32, device=dev)
+    for name, kind, rows, dim in (("ptok_fp8_51x1536", "ptok", 51, 1536),
+                                  ("table_fp8_51x1536", "table", 51, 1536),
+                                  ("ptok_fp8_105x1152", "ptok", 105, 1152),
+                                  ("modulation6_1x51x1536", "mod6", 51, 1536)):
+        if kind == "mod6":
+            d = inputs.make("mod6", batch=1, seq=rows, dim=dim)
+            p, m = f32(d["params"]), f32(d["mod"])
+            outs = [torch.empty((1, rows, dim), dtype=torch.bfloat16, device=dev) for _ in range(6)]
+            arr = (ctypes.c_void_p * 6)(*[o.data_ptr() for o in outs])
+            raw = lambda h: L.alnp_adaln_modulation6_bf16(p.data_ptr(), m.data_ptr(), 1, rows, dim, arr, h)
+            wrap = lambda h: alnp.adaln_modulation6_bf16(p, m, out=outs)
+        elif kind == "ptok":
+            d = inputs.make("ptok", rows=rows, dim=dim)
+            x, sc, sh = bf(d["x"]), bf(d["scale"]), bf(d["shift"])
+            out = torch.empty((rows, dim), dtype=torch.float8_e4m3fn, device=dev)
+            raw = lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_bf16(
+                x.data_ptr(), sc.data_ptr(), sh.data_ptr(), act.data_ptr(), 1e-5, rows, dim,
+                out.data_ptr(), None, None, h)
+            wrap = lambda h: alnp.ada_layer_norm_quant_fp8_ptok_bf16(x, sc, sh, act, out=out)
+        else:
+            d = inputs.make("table", rows=rows, dim=dim)
+            x, te, tb = bf(d["x"]), bf(d["temb"]), f32(d["table"])
+            out = torch.empty((rows, dim), dtype=torch.float8_e4m3fn, device=dev)
+            raw = lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(
+                x.data_ptr(), te.data_ptr(), tb.data_ptr(), 6, 0, 1, act.data_ptr(), 1e-5, rows,
+                dim, out.data_ptr(), None, None, h)
+            wrap = lambda h: alnp.ada_layer_norm_quant_fp8_ptok_table_bf16(x, te, tb, act, 0, 1, out=out)
+
+        def direct(fn):
+            with torch.cuda.stream(stream):
+                h = stream.cuda_stream
+                for _ in range(20):
+                    fn(h)
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                t0.record(stream)
+                for _ in range(calls):
+                    fn(h)
+                t1.record(stream)
+                torch.cuda.synchronize()
+            return t0.elapsed_time(t1) * 1000.0 / calls
+
+        def graphed(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                    hh = torch.cuda.current_stream().cuda_stream
+                    for _ in range(graph_launches):
+                        fn(hh)
+                g.replay()
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record(stream)
+                for _ in range(replays):
+                    g.replay()
+                t1.record(stream)
+                torch.cuda.synchronize()
+            return t0.elapsed_time(t1) * 1000.0 / (replays * graph_launches)
+
+        a1, b1, b2, a2 = direct(raw), direct(wrap), direct(wrap), direct(raw)
+        ga, gb = graphed(raw), graphed(wrap)
+        nat, wr = (a1 + a2) / 2, (b1 + b2) / 2
+        cases[name] = {"native_us": round(nat, 3), "wrapper_us": round(wr, 3),
+                       "graph_native_us": round(ga, 3), "graph_wrapper_us": round(gb, 3),
+                       "wrapper_over_native": round(wr / nat, 3)}
+        print(f"# overhead {name}: native {nat:.3f} us, wrapper {wr:.3f} us, graph native "
+              f"{ga:.3f} us, graph wrapper {gb:.3f} us", file=sys.stderr, flush=True)
+    return cases
+
+
 # ---- counters from rocprofv3 (profiles/) --------------------------------------------
 
 # Sources that build the row-producer kernels (the headline kernel).
@@ -328,6 +416,8 @@ def main():
                      "algorithmic_bytes_per_launch": h["bytes"]},
         "rows": {k: v for k, v in results.items() if k != head},
     }
+    if not a.no_overhead and not a.only_headline and not a.only:
+        line["launch_overhead"] = launch_overhead(torch, alnp, inputs, stream)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_inputs, h["bytes"])
     print(json.dumps(line), flush=True)
