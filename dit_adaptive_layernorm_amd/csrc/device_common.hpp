@@ -73,10 +73,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 
 // ---- e4m3 ----------------------------------------------------------------
 
-// Clamp to the e4m3 range, keeping NaN (the comparison is false for NaN).
+// Clamp to the e4m3 range, keeping NaN: IEEE 754-2019 minimum and maximum
+// (v_minimum3_f32 / v_maximum3_f32), which return NaN for a NaN operand.
 __device__ __forceinline__ float sat448(float v)
 {
-    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+    return __builtin_elementwise_maximum(__builtin_elementwise_minimum(v, 448.0f), -448.0f);
 }
 
 // Four floats (already in range) -> four e4m3 codes, element a in byte 0.
@@ -135,6 +136,41 @@ __device__ __forceinline__ uint32_t pack_e2m1x8(float a, float b, float c, float
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e, f, 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, g, h, 1.0f, 3);
     return w;
+}
+
+// ---- row arithmetic ---------------------------------------------------------
+
+// Partial sum of eight bf16 values: four v_dot2_f32_bf16 against (1, 1),
+// accumulated into `acc` in order.
+__device__ __forceinline__ float sum_bf16x8(const uint4& v, float acc)
+{
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), one, acc, false);
+    return acc;
+}
+
+// 1 / sqrt(v): the hardware reciprocal square root (about 1 ulp) refined by
+// one Newton step r + (r / 2) (1 - v r^2).  v = 0, +inf and NaN keep the
+// hardware result (+inf, 0, NaN), as 1 / sqrt would give.
+__device__ __forceinline__ float rsqrt_refined(float v)
+{
+    const float r = __builtin_amdgcn_rsqf(v);
+    const float e = __builtin_fmaf(-(v * r), r, 1.0f);
+    const float r1 = __builtin_fmaf(0.5f * r, e, r);
+    return (v > 0.f && v < __builtin_inff()) ? r1 : r;
+}
+
+// max(0, |b[0]|, ..., |b[7]|) with NaN operands ignored (fmaxf), as a tree of
+// three-operand maxima.
+__device__ __forceinline__ float absmax8(const float b[8])
+{
+    const float m0 = fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fabsf(b[2]));
+    const float m1 = fmaxf(fmaxf(fabsf(b[3]), fabsf(b[4])), fabsf(b[5]));
+    const float m2 = fmaxf(fmaxf(fabsf(b[6]), fabsf(b[7])), 0.0f);
+    return fmaxf(fmaxf(m0, m1), m2);
 }
 
 // ---- wave reductions ------------------------------------------------------

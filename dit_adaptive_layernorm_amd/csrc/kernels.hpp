@@ -38,6 +38,7 @@ struct Fp8Args {
     uint8_t* out;
     float* row_mean;
     float* row_rstd;
+    float inv_dim;              // 1 / dim in fp32, set by the launcher
 };
 
 // Block-scale layouts of the FP4 producers.
@@ -58,6 +59,7 @@ struct Fp4Args {
     int sf_layout;
     float* row_mean;
     float* row_rstd;
+    float inv_dim;           // 1 / dim in fp32, set by the launcher
 };
 
 struct Mod6Args {

@@ -33,47 +33,51 @@ namespace alnp {
 
 // ---- fast path: one workgroup per row, row held in registers ---------------
 
-// Vector i of a row (eight elements), or zeros past the row end.
+// Vector i of a row (eight elements), or zeros past the row end.  The row
+// shapes put every vector slot but a thread's last inside the row, so only
+// the last (`tail`, a constant once the slot loop is unrolled) is checked.
 template <bool STREAM>
-__device__ __forceinline__ uint4 ld_row(const uint16_t* row, int i, int nvec)
+__device__ __forceinline__ uint4 ld_row(const uint16_t* row, int i, int nvec, bool tail)
 {
-    if (i >= nvec)
+    if (tail && i >= nvec)
         return make_uint4(0, 0, 0, 0);
     return STREAM ? ld_stream(row + 8 * i) : ld_keep(row + 8 * i);
 }
 
 // Row statistics from a thread's VPT register vectors (vector v of thread t is
-// row vector v * nthreads + t).  Zero vectors past the row end add nothing to
-// the sum and are skipped in the squared deviations.
-template <int VPT, int WAVES>
-__device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], int nvec, int dim, float eps,
-                                          float* red, float& mean, float& rstd)
+// row vector v * nthreads + t; only the last slot can lie past the row end,
+// where it holds zeros and `tail_ok` is false).  Two passes over registers:
+// the sum (v_dot2_f32_bf16 against (1, 1)), then the squared deviations from
+// the mean.  mean = sum * (1/dim), var = sum_sq * (1/dim), rstd = 1/sqrt(var
+// + eps), all fp32.  The deviations x - mean are returned in d for the
+// caller's pass over the row.  `reduce` sums a value over the row's waves
+// and takes the slot index (0 or 1) of its LDS partials.
+template <int VPT, typename Reduce>
+__device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], bool tail_ok, float inv_dim,
+                                          float eps, Reduce reduce, float (&d)[VPT][8],
+                                          float& mean, float& rstd)
 {
-    constexpr int nwaves = WAVES;
-    constexpr int nthreads = WAVES * kWave;
     float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        s = sum_bf16x8(xv[v], s);
+    mean = reduce(s, 0) * inv_dim;
+    float q = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         float f[8];
         unpack8(xv[v], f);
-        s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
-    }
-    mean = group_sum(s, red, nwaves) / (float)dim;
-    float q = 0.f;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        if (v * nthreads + (int)threadIdx.x < nvec) {
-            float f[8];
-            unpack8(xv[v], f);
+        for (int e = 0; e < 8; ++e)
+            d[v][e] = f[e] - mean;
+        if (v < VPT - 1 || tail_ok) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = f[e] - mean;
-                q = __builtin_fmaf(d, d, q);
-            }
+            for (int e = 0; e < 8; ++e)
+                q = __builtin_fmaf(d[v][e], d[v][e], q);
         }
     }
-    const float var = group_sum(q, red + 16, nwaves) / (float)dim;
-    rstd = (float)(1.0 / sqrt((double)var + (double)eps));
+    const float var = reduce(q, 1) * inv_dim;
+    rstd = rsqrt_refined(var + eps);
 }
 
 // Row index of a workgroup in the 2-D grid (x fastest); the grid can hold
@@ -81,9 +85,9 @@ __device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], int nvec, int 
 __device__ __forceinline__ int64_t grid_row() { return (int64_t)blockIdx.y * gridDim.x + blockIdx.x; }
 
 // Eight e4m3 operand codes of vector i of a (dim,) byte vector, or zeros.
-__device__ __forceinline__ uint2 ld_fp8x8(const uint8_t* p, int i, int nvec)
+__device__ __forceinline__ uint2 ld_fp8x8(const uint8_t* p, int i, int nvec, bool tail)
 {
-    if (i >= nvec)
+    if (tail && i >= nvec)
         return make_uint2(0, 0);
     return *reinterpret_cast<const uint2*>(p + 8 * i);
 }
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         uint4 xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
+            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, v == VPT - 1);
 
         // Modulation operands, requested before the reductions.  Per-token
         // rows and temb chunks are streamed; (dim,) vectors are shared by
@@ -137,10 +141,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         if (FORM == kBcast || FORM == kAwq) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                scv[v] = ld_row<false>(a.scale, v * T + t, nvec);
-                shv[v] = ld_row<false>(a.shift, v * T + t, nvec);
+                scv[v] = ld_row<false>(a.scale, v * T + t, nvec, v == VPT - 1);
+                shv[v] = ld_row<false>(a.shift, v * T + t, nvec, v == VPT - 1);
                 if (FORM == kAwq)
-                    isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec);
+                    isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, v == VPT - 1);
             }
         } else if (FORM == kPtok || FORM == kTable) {
             const uint16_t* scr = FORM == kPtok ? a.scale + row * dim
@@ -149,29 +153,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                                                 : a.temb + (row * a.chunks + a.shift_idx) * dim;
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                scv[v] = ld_row<true>(scr, v * T + t, nvec);
-                shv[v] = ld_row<true>(shr, v * T + t, nvec);
+                scv[v] = ld_row<true>(scr, v * T + t, nvec, v == VPT - 1);
+                shv[v] = ld_row<true>(shr, v * T + t, nvec, v == VPT - 1);
             }
         } else if (FORM == kModFp8) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec);
-                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec);
+                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, v == VPT - 1);
+                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, v == VPT - 1);
             }
         }
         const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
         const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
 
-        float mean, rstd;
-        row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
+        const bool tail_ok = (VPT - 1) * T + t < nvec;
+        float mean, rstd, d[VPT][8];
+        row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
+                       [&](float v, int k) { return group_sum(v, red + 16 * k, WAVES); }, d, mean,
+                       rstd);
 
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int i = v * T + t;
-            if (i >= nvec)
+            if (v == VPT - 1 && !tail_ok)
                 continue;
-            float f[8], sc[8], sh[8];
-            unpack8(xv[v], f);
+            float sc[8], sh[8];
             if (FORM == kNone) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
             float q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xhat = (f[e] - mean) * rstd;
+                const float xhat = d[v][e] * rstd;
                 float y = (xhat * (1.0f + sc[e])) + sh[e];
                 if (FORM == kAwq)
                     y = y * is[e];  // per-channel smoothing before the static scale
@@ -269,14 +275,16 @@ __global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds
     const uint16_t* xr = a.x + lrow * dim;
     const uint16_t* scr = a.temb + (lrow * a.chunks + a.scale_idx) * dim;
     const uint16_t* shr = a.temb + (lrow * a.chunks + a.shift_idx) * dim;
+    // A workgroup's second row past the end (odd row counts) computes on row 0
+    // and stores nothing.
     uint4 xv[VPT], scv[VPT], shv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-        xv[v] = ld_row<true>(xr, valid ? v * T + t : nvec, nvec);
+        xv[v] = ld_row<true>(xr, v * T + t, nvec, v == VPT - 1);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        scv[v] = ld_row<true>(scr, valid ? v * T + t : nvec, nvec);
-        shv[v] = ld_row<true>(shr, valid ? v * T + t : nvec, nvec);
+        scv[v] = ld_row<true>(scr, v * T + t, nvec, v == VPT - 1);
+        shv[v] = ld_row<true>(shr, v * T + t, nvec, v == VPT - 1);
     }
 
 #pragma unroll
@@ -290,39 +298,20 @@ __global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds
 
     // Row statistics over the row's WAVES waves (the barriers also publish
     // the LDS table).
-    float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        float f[8];
-        unpack8(xv[v], f);
-        s += ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
-    }
-    const float mean = subgroup_sum(s, red[0], rr * WAVES, WAVES) / (float)dim;
-    float q = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        if (v * T + t < nvec) {
-            float f[8];
-            unpack8(xv[v], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = f[e] - mean;
-                q = __builtin_fmaf(d, d, q);
-            }
-        }
-    }
-    const float var = subgroup_sum(q, red[1], rr * WAVES, WAVES) / (float)dim;
-    const float rstd = (float)(1.0 / sqrt((double)var + (double)a.eps));
+    const bool tail_ok = (VPT - 1) * T + t < nvec;
+    float mean, rstd, d[VPT][8];
+    row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
+                   [&](float v, int k) { return subgroup_sum(v, red[k], rr * WAVES, WAVES); }, d,
+                   mean, rstd);
     if (!valid)
         return;
 
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int i = v * T + t;
-        if (i >= nvec)
+        if (v == VPT - 1 && !tail_ok)
             continue;
-        float f[8], sc[8], sh[8];
-        unpack8(xv[v], f);
+        float sc[8], sh[8];
         unpack8(scv[v], sc);
         unpack8(shv[v], sh);
         const float4 s0 = tab[2 * i], s1 = tab[2 * i + 1];
@@ -334,7 +323,7 @@ __global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds
         for (int e = 0; e < 8; ++e) {
             const float scale = sc[e] + ts[e];
             const float shift = sh[e] + th[e];
-            const float xhat = (f[e] - mean) * rstd;
+            const float xhat = d[v][e] * rstd;
             const float y = (xhat * (1.0f + scale)) + shift;
             q8[e] = sat448(y * inv);
         }
@@ -375,6 +364,24 @@ __device__ __forceinline__ void store_scale(uint8_t* sf, int64_t row, int c, int
             sf[sf_swizzled_offset(row, p, cols)] = 0;
 }
 
+// 1 / s for every e4m3 code s below 0x7F (0 for code 0), rounded to nearest
+// even by the compiler's constant evaluation (IEEE binary32 division).
+struct E4m3Recip {
+    float v[128];
+    constexpr E4m3Recip() : v()
+    {
+        for (int c = 1; c < 127; ++c) {
+            const int e = (c >> 3) & 15, m = c & 7;
+            float p = 1.0f;  // 2^e
+            for (int k = 0; k < e; ++k)
+                p *= 2.0f;
+            const float s = e == 0 ? (float)m / 512.0f : (float)(8 + m) * p / 1024.0f;
+            v[c] = 1.0f / s;
+        }
+    }
+};
+__device__ const E4m3Recip kE4m3Recip{};
+
 // LayerNorm (MOD = false) or broadcast AdaLN (MOD = true) -> FP4.
 template <int VPT, int WAVES, bool MOD, bool SWZ>
 __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
@@ -390,26 +397,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
     const int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
-    // The encode factor 1 / s is an IEEE division per scale code; tabulate it
-    // once per workgroup instead of once per block.
-    for (int c = t; c < 128; c += T)
-        inv_s[c] = (c == 0 || c == 127) ? 0.f : 1.0f / e4m3_value((uint32_t)c);
+    // The encode factors 1 / s, staged from the compile-time table into LDS
+    // (requested here, written once the row loads are in flight).
+    const float recip0 = t < 128 ? kE4m3Recip.v[t] : 0.f;
+    const float recip1 = T == 64 ? kE4m3Recip.v[t + 64] : 0.f;
 
     uint4 xv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-        xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec);
+        xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, v == VPT - 1);
     uint4 scv[NM], shv[NM];
     if (MOD) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            scv[v] = ld_row<false>(a.scale, v * T + t, nvec);
-            shv[v] = ld_row<false>(a.shift, v * T + t, nvec);
+            scv[v] = ld_row<false>(a.scale, v * T + t, nvec, v == VPT - 1);
+            shv[v] = ld_row<false>(a.shift, v * T + t, nvec, v == VPT - 1);
         }
     }
+    if (t < 128)
+        inv_s[t] = recip0;
+    if (T == 64)
+        inv_s[t + 64] = recip1;
 
-    float mean, rstd;
-    row_stats<VPT, WAVES>(xv, nvec, dim, a.eps, red, mean, rstd);
+    const bool tail_ok = (VPT - 1) * T + t < nvec;
+    float mean, rstd, d[VPT][8];
+    row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
+                   [&](float v, int k) { return group_sum(v, red + 16 * k, WAVES); }, d, mean,
+                   rstd);
     if (WAVES == 1)
         __syncthreads();  // inv_s visible (row_stats has no barrier for one wave)
 
@@ -424,44 +438,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
         // (T is a multiple of 64 and nvec is even, so both lanes of a pair
         // take the same branch).
         const int i = v * T + t;
-        if (i >= nvec)
+        if (v == VPT - 1 && !tail_ok)
             continue;
-        float f[8], b[8], y[8];
-        unpack8(xv[v], f);
+        float b[8], y[8];
         if (MOD) {
             float sc[8], sh[8];
             unpack8(scv[v], sc);
             unpack8(shv[v], sh);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xhat = (f[e] - mean) * rstd;
+                const float xhat = d[v][e] * rstd;
                 y[e] = (xhat * (1.0f + sc[e])) + sh[e];
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                y[e] = (f[e] - mean) * rstd;
+                y[e] = d[v][e] * rstd;
         }
-        float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             // Stage through bf16 (round to nearest even).
             const uint32_t w = pack_bf16x2(y[e], y[e + 1]);
             b[e] = bf16_lo(w);
             b[e + 1] = bf16_hi(w);
-            amax = fmaxf(amax, fmaxf(fabsf(b[e]), fabsf(b[e + 1])));
         }
-        amax = pair_max(amax);
+        const float amax = pair_max(absmax8(b));
         const uint32_t scode = pack_e4m3x4(fminf(amax * kSixth, 448.0f), 0.f, 0.f, 0.f) & 0xFFu;
-        uint32_t word = 0;
-        if (scode != 0) {
-            const float enc = inv_s[scode];
-            word = pack_e2m1x8(b[0] * enc, b[1] * enc, b[2] * enc, b[3] * enc,
-                               b[4] * enc, b[5] * enc, b[6] * enc, b[7] * enc);
-        }
-        st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
-        if ((t & 1) == 0)
-            store_scale<SWZ>(a.sf, row, i >> 1, cols, (uint8_t)scode);
+        // A zero scale gives zero codes (a select, not a branch: inv_s[0] is
+        // 0 and would leave the signs of negative values).
+        const float enc = inv_s[scode];
+        const uint32_t word = pack_e2m1x8(b[0] * enc, b[1] * enc, b[2] * enc, b[3] * enc,
+                                          b[4] * enc, b[5] * enc, b[6] * enc, b[7] * enc);
+        st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, scode != 0 ? word : 0u);
+        // Both lanes of the pair hold the block's scale and store the same
+        // byte (no lane condition).
+        store_scale<SWZ>(a.sf, row, i >> 1, cols, (uint8_t)scode);
     }
     if (t == 0) {
         if (a.row_mean) a.row_mean[row] = mean;
@@ -488,20 +499,21 @@ __device__ __forceinline__ float ldbf(const uint16_t* p, int64_t i)
     return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-__device__ __forceinline__ void block_row_stats(const uint16_t* xr, int dim, float eps,
-                                                float* lds4, float& mean, float& rstd)
+__device__ __forceinline__ void block_row_stats(const uint16_t* xr, int dim, float inv_dim,
+                                                float eps, float* lds4, float& mean,
+                                                float& rstd)
 {
     float s = 0.f;
     for (int j = threadIdx.x; j < dim; j += 256)
         s += ldbf(xr, j);
-    mean = block_sum(s, lds4) / (float)dim;
+    mean = block_sum(s, lds4) * inv_dim;
     float q = 0.f;
     for (int j = threadIdx.x; j < dim; j += 256) {
         const float d = ldbf(xr, j) - mean;
         q = __builtin_fmaf(d, d, q);
     }
-    const float var = block_sum(q, lds4) / (float)dim;
-    rstd = (float)(1.0 / sqrt((double)var + (double)eps));
+    const float var = block_sum(q, lds4) * inv_dim;
+    rstd = rsqrt_refined(var + eps);
 }
 
 __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const uint16_t* xr = a.x + row * dim;
     float mean, rstd;
-    block_row_stats(xr, dim, a.eps, lds4, mean, rstd);
+    block_row_stats(xr, dim, a.inv_dim, a.eps, lds4, mean, rstd);
     for (int j = threadIdx.x; j < dim; j += 256) {
         float sc = 0.f, sh = 0.f;
         if (form == kBcast) {
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(256) void k_fp4_block(Fp4Args a)
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const uint16_t* xr = a.x + row * dim;
     float mean, rstd;
-    block_row_stats(xr, dim, a.eps, lds4, mean, rstd);
+    block_row_stats(xr, dim, a.inv_dim, a.eps, lds4, mean, rstd);
     for (int k = threadIdx.x; k < dim / 16; k += 256) {
         float b[16];
         float amax = 0.f;
@@ -627,8 +639,8 @@ RowShape row_shape(int dim)
         int waves = 1;
         while (waves * 64 * vpt < nvec && waves < 8)
             waves *= 2;
-        if (waves * 64 * vpt < nvec)
-            continue;
+        if (waves * 64 * vpt < nvec || (vpt - 1) * waves * 64 > nvec)
+            continue;  // too short, or more than the last slot past the end
         const double waste = double(waves * 64 * vpt - nvec) / nvec;
         const double score = waste + (vpt == 1 ? 0.1 : vpt > 4 ? 0.02 * (vpt - 4) : 0.0) +
                              (vpt == 3 ? -1e-3 : 0.0);
@@ -680,19 +692,29 @@ static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
     return hipGetLastError();
 }
 
+// The LDS table kernel runs rows of at most 4 waves (its caller checks), so
+// the 8-wave shapes are not instantiated.
+template <int V, int W>
+static void launch_table_lds_shape(const Fp8Args& a, dim3 grid, size_t lds, hipStream_t s)
+{
+    if constexpr (W <= 4)
+        hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W>), grid, dim3(kTableRows * W * 64), lds, s, a);
+}
+
 static hipError_t launch_fp8_table_lds(const Fp8Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid((a.rows + kTableRows - 1) / kTableRows);
     const size_t lds = 2 * (size_t)a.dim * sizeof(float);
-#define ALNP_LAUNCH(V, W) \
-    hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W>), grid, dim3(kTableRows * W * 64), lds, s, a)
+#define ALNP_LAUNCH(V, W) launch_table_lds_shape<V, W>(a, grid, lds, s)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)
 #undef ALNP_LAUNCH
     return hipGetLastError();
 }
 
-hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s)
+hipError_t launch_adaln_fp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
 {
+    Fp8Args a = args;
+    a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
     if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256)
         return launch_fp8_table_lds(a, rs, s);
@@ -722,8 +744,10 @@ static hipError_t launch_fp4_rows(const Fp4Args& a, RowShape rs, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_fp4(const Fp4Args& a, bool fast, hipStream_t s)
+hipError_t launch_fp4(const Fp4Args& args, bool fast, hipStream_t s)
 {
+    Fp4Args a = args;
+    a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
     if (rs.vpt > 0) {
         const bool mod = a.scale != nullptr, swz = a.sf_layout == kSfSwizzled;

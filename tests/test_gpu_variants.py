@@ -152,6 +152,40 @@ def test_adaln_fp4_rowmajor_shapes(orc, rows, dim):
     fp4_check(host_u8(packed), host_u8(sf), rp, rs, f"adaln fp4 {rows}x{dim}")
 
 
+def test_adaln_fp4_every_scale_code(orc):
+    # Per-block modulation factors 1 + scale log-spaced over 2^-8 .. 2^10 spread
+    # the block maxima so that every e4m3 scale code 0..126 occurs (asserted on
+    # the oracle's output), which exercises the kernel's 1/s for each code.
+    rows, dim = 64, 4096
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=11)
+    nb = dim // 16
+    u = -8.0 + 18.0 * np.arange(nb) / (nb - 1)
+    scale = inputs.to_bf16_bits(np.repeat(2.0 ** u - 1.0, 16).astype(np.float32))
+    shift = np.zeros(dim, np.uint16)
+    rp, rs, _, _, _ = orc.adaln_fp4(d["x"], scale, shift)
+    assert set(np.unique(rs).tolist()) == set(range(127))
+    packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(dev_bf16(d["x"]), dev_bf16(scale), dev_bf16(shift))
+    fp4_check(host_u8(packed), host_u8(sf), rp, rs, "every scale code")
+
+
+def test_fp4_non_finite_rows(orc):
+    # A NaN or an infinity in a row makes its statistics NaN; every block
+    # maximum then ignores the NaN values, so the row gets zero scales and
+    # zero codes, as in the oracle.  The other rows are unaffected.
+    rows, dim = 4, 3072
+    d = inputs.make("fp4", rows=rows, dim=dim, seed=12)
+    xb = d["x"].copy()
+    xb[1, 100] = 0x7FC0   # NaN
+    xb[2, 7] = 0x7F80     # +inf
+    xb[3, 3000] = 0xFF80  # -inf
+    packed, sf = alnp.layer_norm_no_affine_quant_nvfp4_bf16(dev_bf16(xb))
+    rp, rs, _, _, _ = orc.ln_fp4(xb)
+    gp, gs = host_u8(packed), host_u8(sf)
+    assert np.all(rp[1:] == 0) and np.all(rs[1:] == 0)
+    assert np.array_equal(gp[1:], rp[1:]) and np.array_equal(gs[1:], rs[1:])
+    fp4_check(gp[:1], gs[:1], rp[:1], rs[:1], "finite row")
+
+
 @pytest.mark.parametrize("mod", [False, True])
 @pytest.mark.parametrize("rows,dim", [(1, 3072), (130, 3072), (129, 80), (7, 48), (2, 32784),
                                       (300, 1536)])
