@@ -90,11 +90,27 @@ def _check(fn: str, status: int) -> None:
         raise AlnpError(fn, status)
 
 
+# The raw current stream of the current device, read without building a
+# torch.cuda.Stream object (which costs microseconds per call).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream() -> int:
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
     return torch.cuda.current_stream().cuda_stream
 
 
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
+    """Device pointer of a contiguous GPU tensor of the given dtype (and
+    shape); raises with the reason otherwise."""
+    try:
+        if (t.dtype is dtype and t.is_cuda and t.is_contiguous()
+                and (shape is None or t.shape == shape)):
+            return t.data_ptr()
+    except AttributeError:
+        pass
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -113,16 +129,17 @@ def _opt(t, name, shape):
 
 
 def _x(x):
+    _dev(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise ValueError("x must be 2-D (rows, dim)")
-    _dev(x, "x", torch.bfloat16)
     return x.shape
 
 
 def _act(act_scale):
+    p = _dev(act_scale, "act_scale", torch.float32)
     if act_scale.numel() != 1:
         raise ValueError("act_scale must hold one fp32 value")
-    return _dev(act_scale, "act_scale", torch.float32, act_scale.shape)
+    return p
 
 
 def _fp8_out(out, x):
@@ -180,9 +197,10 @@ def ada_layer_norm_quant_fp8_ptok_table_bf16(x, temb, table, act_scale, shift_id
 
 
 def _scalar(t, name):
+    p = _dev(t, name, torch.float32)
     if t.numel() != 1:
         raise ValueError(f"{name} must hold one fp32 value")
-    return _dev(t, name, torch.float32, t.shape)
+    return p
 
 
 def ada_layer_norm_quant_fp8_modfp8_bf16(x, scale_fp8, shift_fp8, scale_deq, shift_deq,
