@@ -15,6 +15,12 @@ modulation producer at B1 S5070 D3072) with value distributions chosen per
 workload: activations N(0, 1), modulation operands N(0, 0.1), timestep
 embedding chunks N(0, 0.5), and for the FP4 producer a 1% Bernoulli mask of
 x20 outliers applied before the bf16 rounding.
+
+The RMSNorm-modulation producer runs at the h3 page's canonical hidden shape,
+37810 tokens x 5376, with its request layout of three segments (tokens
+[0, 100) use modulation row 1, [100, 514) row 2, the rest row 0): RMSNorm
+weight 1 + N(0, 0.1), scale/shift tables (3, dim) N(0, 0.1).  Small parity
+cases draw each row's segment uniformly instead.
 """
 from __future__ import annotations
 
@@ -23,7 +29,7 @@ import torch
 
 # One stream id per tensor role, so that adding a tensor never shifts another.
 STREAM = {"x": 1, "scale": 2, "shift": 3, "temb": 4, "table": 5, "params": 6,
-          "mod": 7, "outlier": 8}
+          "mod": 7, "outlier": 8, "weight": 9, "seg": 10}
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -65,17 +71,38 @@ WORKLOADS = {
                                 shift_idx=0, scale_idx=1),
     "modulation6_1x5070x3072": dict(kind="mod6", batch=1, seq=5070, dim=3072),
     "ln_fp4_4096x3072": dict(kind="fp4", rows=4096, dim=3072),
+    "rmsmod_bf16_37810x5376": dict(kind="rmsmod", rows=37810, dim=5376, segments=3,
+                                   layout="h3"),
 }
+
+# The h3 page's request layout: (first token, end token, modulation row).
+H3_SEGMENTS = ((0, 100, 1), (100, 514, 2), (514, None, 0))
+
+
+def segment_ids(rows: int, segments: int, layout: str, seed: int) -> np.ndarray:
+    """Per-row modulation row index (int32): the h3 layout, or uniform draws."""
+    if layout == "h3":
+        seg = np.zeros(rows, np.int32)
+        for a, b, k in H3_SEGMENTS:
+            seg[a:rows if b is None else min(b, rows)] = k
+        return seg
+    return rng(seed, STREAM["seg"]).integers(0, segments, rows).astype(np.int32)
 
 
 def make(kind: str, seed: int = 0, rows: int = 0, dim: int = 0, chunks: int = 6,
          shift_idx: int = 0, scale_idx: int = 1, batch: int = 1, seq: int = 0,
-         outliers: bool = True) -> dict:
+         outliers: bool = True, segments: int = 3, layout: str = "random") -> dict:
     """Inputs for one producer at any shape, same distributions as above.
 
-    kind: "ln" | "bcast" | "ptok" | "table" | "fp4" | "mod6".
+    kind: "ln" | "bcast" | "ptok" | "table" | "fp4" | "mod6" | "rmsmod".
     """
     s = STREAM
+    if kind == "rmsmod":
+        w = (normal_f32((dim,), 0.1, seed, s["weight"]) + np.float32(1.0)).astype(np.float32)
+        return dict(x=normal_bf16((rows, dim), 1.0, seed, s["x"]), weight=to_bf16_bits(w),
+                    scale=normal_bf16((segments, dim), 0.1, seed, s["scale"]),
+                    shift=normal_bf16((segments, dim), 0.1, seed, s["shift"]),
+                    seg=segment_ids(rows, segments, layout, seed), eps=EPS)
     if kind == "mod6":
         return dict(params=normal_f32((batch, seq, 6, dim), 1.0, seed, s["params"]),
                     mod=normal_f32((6, dim), 0.1, seed, s["mod"]))

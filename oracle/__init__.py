@@ -47,6 +47,8 @@ _SIGS = {
     "orc_adaln_fp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
     "orc_sf_swizzle": [_P, _I64, _I64, _P],
     "orc_gated_residual": [_P, _P, _P, _I64, _I64, _I64, _P],
+    "orc_bf16_modulate_n": [_P, _P, _P, _I64, _P],
+    "orc_rms_modulate_seg": [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P],
 }
 
 _RESTYPES = {"orc_sf_swizzled_size": ([_I64, _I64], _I64),
@@ -384,6 +386,46 @@ def gated_residual(residual, gate, proj):
     out = np.empty((rows, dim), np.uint16)
     lib().orc_gated_residual(_ptr(res), _ptr(g), _ptr(pr), rows, dim, gate_rows, _ptr(out))
     return out
+
+
+# ---- RMSNorm with segment-selected modulation (R14) -------------------------
+
+def bf16_modulate(n, scale, shift):
+    """Elementwise bf16((bf16(n * bf16(scale + 1))) + shift) on bf16 bits of one shape."""
+    n = _c(n, np.uint16)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    assert n.shape == scale.shape == shift.shape
+    out = np.empty(n.shape, np.uint16)
+    lib().orc_bf16_modulate_n(_ptr(n), _ptr(scale), _ptr(shift), n.size, _ptr(out))
+    return out
+
+
+def rms_modulate_seg(x, weight, scale, shift, seg, eps=1e-5, want_n=False, threads=1):
+    """RMSNorm (weight (dim,) or None) then (n * (scale[seg] + 1)) + shift[seg]
+    in bf16 operations.  scale, shift (segments, dim) bf16; seg (rows,) int32.
+    Returns (out (rows, dim) bf16 bits, rstd (rows,), n or None)."""
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    w = None if weight is None else _c(weight, np.uint16)
+    assert w is None or w.shape == (dim,)
+    scale = _c(scale, np.uint16)
+    shift = _c(shift, np.uint16)
+    segments = scale.shape[0]
+    assert scale.shape == shift.shape == (segments, dim)
+    seg = _c(seg, np.int32)
+    assert seg.shape == (rows,)
+    out = np.empty((rows, dim), np.uint16)
+    rstd = np.empty(rows, np.float32)
+    n = np.empty((rows, dim), np.uint16) if want_n else None
+
+    def run(r0, r1):
+        lib().orc_rms_modulate_seg(_rowptr(x, r0, dim), None if w is None else _ptr(w),
+                                   _ptr(scale), _ptr(shift), _rowptr(seg, r0, 1), segments,
+                                   eps, r1 - r0, dim, _rowptr(out, r0, dim),
+                                   _rowptr(rstd, r0, 1), _rowptr(n, r0, dim))
+    _parallel(rows, threads, run)
+    return out, rstd, n
 
 
 # ---- six-way modulation ---------------------------------------------------

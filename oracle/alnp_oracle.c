@@ -46,6 +46,18 @@
  *      program: bf16 GEMM output, gate multiplication with its bf16
  *      boundary, bf16 residual added, final bf16 rounding):
  *      out = bf16(residual + bf16(gate * proj)), fp32 arithmetic.
+ *  R14 RMSNorm modulation (RL-Kernel norm_modulate page: modulated RMSNorm
+ *      with a weight and index-selected scale/shift rows; h3 page, "NVFP4
+ *      Modulation Producer Fusion", "Exactness Contract": segment-specific
+ *      scale and shift, (x * (scale + 1)) + shift order, BF16 rounding):
+ *      rstd = 1/sqrt(sum(x^2)/dim + eps), mean of squares with no centring,
+ *      in double, rounded once to fp32.  The RMSNorm output is a bf16
+ *      tensor: n = bf16((x * rstd) * w), two fp32 operations (w = 1 when
+ *      absent).  Each modulation operation is a bf16 tensor operation,
+ *      computed in fp32 and rounded once: t = bf16(scale + 1),
+ *      u = bf16(n * t), y = bf16(u + shift).  scale and shift are rows seg[r]
+ *      of (segments, dim) tables; a row whose index is outside [0, segments)
+ *      is all NaN (0x7FC0).
  */
 #include "alnp_oracle.h"
 
@@ -587,4 +599,57 @@ void orc_modulation6(const float* params, const float* mod, int64_t tokens,
                 float s = params[(t * 6 + k) * dim + j] + mod[k * dim + j];
                 out[(k * tokens + t) * dim + j] = orc_f32_to_bf16(s);
             }
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm with segment-selected modulation (R14).                            */
+/* ------------------------------------------------------------------------ */
+
+float orc_rms_rstd(const uint16_t* xr, int64_t dim, float eps)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < dim; ++j) {
+        double v = (double)orc_bf16_to_f32(xr[j]);
+        ss += v * v;
+    }
+    return (float)(1.0 / sqrt(ss / (double)dim + (double)eps));
+}
+
+uint16_t orc_bf16_modulate(uint16_t n, uint16_t scale, uint16_t shift)
+{
+    float t = orc_bf16_to_f32(orc_f32_to_bf16(orc_bf16_to_f32(scale) + 1.0f));
+    float u = orc_bf16_to_f32(orc_f32_to_bf16(orc_bf16_to_f32(n) * t));
+    return orc_f32_to_bf16(u + orc_bf16_to_f32(shift));
+}
+
+void orc_bf16_modulate_n(const uint16_t* n, const uint16_t* scale, const uint16_t* shift,
+                         int64_t count, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = orc_bf16_modulate(n[i], scale[i], shift[i]);
+}
+
+void orc_rms_modulate_seg(const uint16_t* x, const uint16_t* weight, const uint16_t* scale,
+                          const uint16_t* shift, const int32_t* seg, int64_t segments,
+                          float eps, int64_t rows, int64_t dim, uint16_t* out,
+                          float* rstd_out, uint16_t* n_out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        float rstd = orc_rms_rstd(xr, dim, eps);
+        if (rstd_out)
+            rstd_out[r] = rstd;
+        int64_t s = seg[r];
+        int in_range = s >= 0 && s < segments;
+        for (int64_t j = 0; j < dim; ++j) {
+            float v = orc_bf16_to_f32(xr[j]) * rstd;
+            if (weight)
+                v = v * orc_bf16_to_f32(weight[j]);
+            uint16_t n = orc_f32_to_bf16(v);
+            if (n_out)
+                n_out[r * dim + j] = n;
+            out[r * dim + j] = in_range ? orc_bf16_modulate(n, scale[s * dim + j], shift[s * dim + j])
+                                        : (uint16_t)0x7FC0;
+        }
+    }
 }

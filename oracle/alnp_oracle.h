@@ -140,6 +140,21 @@ void orc_gated_residual(const uint16_t* residual, const uint16_t* gate,
 void orc_modulation6(const float* params, const float* mod, int64_t tokens,
                      int64_t dim, uint16_t* out);
 
+/* ---- RMSNorm with segment-selected modulation (R14) ----------------------- */
+/* rstd of one row: 1/sqrt(sum(x^2)/dim + eps), double, rounded to fp32. */
+float orc_rms_rstd(const uint16_t* xr, int64_t dim, float eps);
+/* bf16((bf16(n * bf16(scale + 1))) + shift), each operation fp32 then bf16. */
+uint16_t orc_bf16_modulate(uint16_t n, uint16_t scale, uint16_t shift);
+void orc_bf16_modulate_n(const uint16_t* n, const uint16_t* scale, const uint16_t* shift,
+                         int64_t count, uint16_t* out);
+/* x (rows, dim) bf16; weight (dim,) bf16 or NULL; scale, shift (segments, dim)
+ * bf16; seg (rows,) int32 -> out (rows, dim) bf16, rstd (rows,) (nullable),
+ * n = the bf16 RMSNorm output (rows, dim) (nullable test hook). */
+void orc_rms_modulate_seg(const uint16_t* x, const uint16_t* weight, const uint16_t* scale,
+                          const uint16_t* shift, const int32_t* seg, int64_t segments,
+                          float eps, int64_t rows, int64_t dim, uint16_t* out,
+                          float* rstd_out, uint16_t* n_out);
+
 #ifdef __cplusplus
 }
 #endif
