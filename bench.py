@@ -71,6 +71,10 @@ def algorithmic_bytes(name, d):
         return p.nbytes + d["mod"].nbytes + p.size // 6 * 6 * 2
     x = d["x"]
     rows, dim = x.shape
+    if name.startswith("rmsmod"):
+        # x, bf16 out, the weight, the table rows the segments use, the indices
+        used = len(np.unique(d["seg"]))
+        return 2 * x.nbytes + dim * 2 + used * 2 * dim * 2 + rows * 4
     if name.startswith("ln_fp4"):
         return x.nbytes + rows * dim // 2 + rows * dim // 16
     b = x.nbytes + rows * dim + 4  # x, e4m3 out, act_scale
@@ -110,6 +114,18 @@ class Producer:
             return
         x0 = bf(d["x"])
         rows, dim = x0.shape
+        if kind == "rmsmod":
+            w, sc, sh = bf(d["weight"]), bf(d["scale"]), bf(d["shift"])
+            seg = torch.from_numpy(d["seg"]).to(dev)
+            for _ in range(sets):
+                x = x0.clone()
+                out = torch.empty_like(x)
+                self.keep.append((x, out, w, sc, sh, seg))
+                self.calls.append((self.L.alnp_rms_norm_modulate_seg_bf16,
+                                   (x.data_ptr(), w.data_ptr(), sc.data_ptr(), sh.data_ptr(),
+                                    seg.data_ptr(), sc.shape[0], d["eps"], rows, dim,
+                                    out.data_ptr(), None)))
+            return
         act0 = torch.tensor([d.get("act_scale", 0.025)], dtype=torch.float32, device=dev)
         ops = {}
         if kind in ("bcast", "ptok"):
@@ -353,7 +369,7 @@ def main():
     head = "ptok_fp8_2520x3072"
     names = [head] if a.only_headline else [
         head, "table_fp8_2520x3072", "bcast_fp8_16x2048", "ln_fp8_2520x3072",
-        "ln_fp4_4096x3072", "modulation6_1x5070x3072"]
+        "ln_fp4_4096x3072", "modulation6_1x5070x3072", "rmsmod_bf16_37810x5376"]
     if a.only:
         names = [n for n in a.only.split(",") if n]
     modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]

@@ -55,6 +55,8 @@ SIGNATURES = {
         [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_swizzled_sf_size": ([_I64, _I64], _I64),
     "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
+    "alnp_rms_norm_modulate_seg_bf16": (
+        [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P], _I),
 }
 
 STATUS = {0: "ALNP_OK", -1: "ALNP_ERR_NULL", -2: "ALNP_ERR_SHAPE", -3: "ALNP_ERR_DIM",
@@ -394,6 +396,29 @@ def gated_residual_bf16(residual, gate, proj, out=None):
     return out
 
 
+# ---- RMSNorm with segment-selected modulation -------------------------------------
+
+def rms_norm_modulate_seg_bf16(x, weight, scale, shift, seg, eps=1e-5, out=None, row_rstd=None):
+    """RMSNorm (weight (dim,) bf16 or None) then (n * (scale[seg] + 1)) + shift[seg]
+    in bf16 operations.  scale, shift (segments, dim) bf16; seg (rows,) int32
+    table row per row (outside [0, segments): NaN row).  Returns out (rows, dim)
+    bf16."""
+    rows, dim = _x(x)
+    if scale.dim() != 2:
+        raise ValueError("scale must be (segments, dim)")
+    segments = scale.shape[0]
+    wp = None if weight is None else _dev(weight, "weight", torch.bfloat16, (dim,))
+    if out is None:
+        out = torch.empty_like(x)
+    _check("alnp_rms_norm_modulate_seg_bf16", lib().alnp_rms_norm_modulate_seg_bf16(
+        x.data_ptr(), wp, _dev(scale, "scale", torch.bfloat16, (segments, dim)),
+        _dev(shift, "shift", torch.bfloat16, (segments, dim)),
+        _dev(seg, "seg", torch.int32, (rows,)), segments, eps, rows, dim,
+        _dev(out, "out", torch.bfloat16, (rows, dim)), _opt(row_rstd, "row_rstd", (rows,)),
+        _stream()))
+    return out
+
+
 # ---- standalone quantizer --------------------------------------------------------
 
 def quant_fp8_static_f32(v, act_scale, out=None):
@@ -414,6 +439,6 @@ __all__ = [
     "layer_norm_no_affine_quant_nvfp4_bf16", "layer_norm_no_affine_quant_nvfp4_swizzled_bf16",
     "ada_layer_norm_quant_nvfp4_bf16", "ada_layer_norm_quant_nvfp4_swizzled_bf16",
     "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "gated_residual_bf16",
-    "quant_fp8_static_f32",
+    "rms_norm_modulate_seg_bf16", "quant_fp8_static_f32",
     "lib", "AlnpError", "SIGNATURES",
 ]

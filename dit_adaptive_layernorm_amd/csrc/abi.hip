@@ -320,6 +320,32 @@ int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
     return launch_status(alnp::launch_gated_residual(a, fast, as_stream(stream)));
 }
 
+int alnp_rms_norm_modulate_seg_bf16(const uint16_t* x, const uint16_t* weight,
+                                    const uint16_t* scale, const uint16_t* shift,
+                                    const int32_t* seg, int64_t segments, float eps,
+                                    int64_t rows, int64_t dim, uint16_t* out, float* row_rstd,
+                                    void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 1))
+        return st > 0 ? ALNP_OK : st;
+    if (segments < 1 || segments > INT32_MAX)
+        return ALNP_ERR_SHAPE;
+    if (!x || !scale || !shift || !seg || !out)
+        return ALNP_ERR_NULL;
+    if (!aligned(x, 2) || (weight && !aligned(weight, 2)) || !aligned(scale, 2) ||
+        !aligned(shift, 2) || !aligned(seg, 4) || !aligned(out, 2) ||
+        (row_rstd && !aligned(row_rstd, 4)))
+        return ALNP_ERR_ALIGN;
+    if (int st = check_eps(eps))
+        return st;
+    alnp::RmsArgs a{x, weight, scale, shift, seg, segments, eps, rows, (int)dim, out, row_rstd,
+                    0.f};
+    const bool fast = dim % 8 == 0 && dim <= alnp::kMaxFastDim && aligned(x, 16) &&
+                      (!weight || aligned(weight, 16)) && aligned(scale, 16) &&
+                      aligned(shift, 16) && aligned(out, 16);
+    return launch_status(alnp::launch_rms_modulate(a, fast, as_stream(stream)));
+}
+
 int alnp_quant_fp8_static_f32(const float* v, const float* act_scale, int64_t n, uint8_t* out,
                               void* stream)
 {

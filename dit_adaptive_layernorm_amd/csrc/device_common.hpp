@@ -152,6 +152,17 @@ __device__ __forceinline__ float sum_bf16x8(const uint4& v, float acc)
     return acc;
 }
 
+// Partial sum of squares of eight bf16 values: v_dot2_f32_bf16 of each pair
+// with itself (the products are exact in fp32).
+__device__ __forceinline__ float sumsq_bf16x8(const uint4& v, float acc)
+{
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, v.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, v.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, v.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, v.w), acc, false);
+    return acc;
+}
+
 // 1 / sqrt(v): the hardware reciprocal square root (about 1 ulp) refined by
 // one Newton step r + (r / 2) (1 - v r^2).  v = 0, +inf and NaN keep the
 // hardware result (+inf, 0, NaN), as 1 / sqrt would give.

@@ -80,6 +80,21 @@ struct GateArgs {
     uint16_t* out;             // (rows, dim), may be residual
 };
 
+struct RmsArgs {
+    const uint16_t* x;         // (rows, dim)
+    const uint16_t* weight;    // (dim,) or null
+    const uint16_t* scale;     // (segments, dim)
+    const uint16_t* shift;     // (segments, dim)
+    const int32_t* seg;        // (rows,) table row per row
+    int64_t segments;
+    float eps;
+    int64_t rows;
+    int dim;
+    uint16_t* out;             // (rows, dim)
+    float* row_rstd;           // (rows,) or null
+    float inv_dim;             // 1 / dim in fp32, set by the launcher
+};
+
 // Largest row (elements) the register-resident row kernels take: 8 waves,
 // 8 vectors of 8 elements per thread.
 constexpr int kMaxFastDim = 8 * 64 * 8 * 8;
@@ -110,5 +125,7 @@ hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
 hipError_t launch_gated_residual(const GateArgs& a, bool fast, hipStream_t s);
 hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t* out,
                             hipStream_t s);
+// fast: as for launch_adaln_fp8 (x, out, weight and tables 16-byte aligned).
+hipError_t launch_rms_modulate(const RmsArgs& a, bool fast, hipStream_t s);
 
 }  // namespace alnp

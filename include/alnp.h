@@ -262,6 +262,38 @@ int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
                              int64_t gate_rows, uint16_t* out, void* stream);
 
 /*
+ * RMSNorm with segment-selected AdaLN modulation -> bf16.  Sources: the
+ * RL-Kernel norm_modulate page (a modulated RMSNorm with an RMSNorm weight and
+ * scale/shift rows picked per token by index_select) and the
+ * h3-blackwell-runtime page ("Implementation Phases": RMSNorm output plus
+ * segmented AdaLN scale/shift modulation; "NVFP4 Modulation Producer
+ * Fusion", "Exactness Contract": segment-specific scale and shift, the
+ * (x * (scale + 1)) + shift order, BF16 rounding).  Per row r, s = seg[r]:
+ *   rstd = 1 / sqrt(sum_j x[r, j]^2 / dim + eps)     (fp32; no centring)
+ *   n    = bf16_rne((x * rstd) * weight[j])          (weight 1 if NULL)
+ *   t    = bf16_rne(scale[s, j] + 1)
+ *   u    = bf16_rne(n * t)
+ *   out  = bf16_rne(u + shift[s, j])
+ * Every bf16 step is one fp32 operation rounded to bf16, as a bf16 tensor
+ * operation is.
+ *   x             (rows, dim) bf16
+ *   weight        (dim,) bf16, or NULL for no RMSNorm weight
+ *   scale, shift  (segments, dim) bf16 tables, segments >= 1
+ *   seg           (rows,) int32 table row of each row (DEVICE; not read on the
+ *                 host).  A row whose index is outside [0, segments) reads no
+ *                 table row and is written as quiet NaN (0x7FC0).
+ *   out           (rows, dim) bf16
+ *   row_rstd      (rows,) fp32 or NULL
+ * Any dim in 1 .. 2^24 (no parity rule); segments outside 1 .. 2^31 - 1
+ * returns ALNP_ERR_SHAPE.
+ */
+int alnp_rms_norm_modulate_seg_bf16(const uint16_t* x, const uint16_t* weight,
+                                    const uint16_t* scale, const uint16_t* shift,
+                                    const int32_t* seg, int64_t segments, float eps,
+                                    int64_t rows, int64_t dim, uint16_t* out,
+                                    float* row_rstd, void* stream);
+
+/*
  * Static-scale FP8 quantizer on its own, the last stage of every FP8
  * producer: out[i] = e4m3(v[i] * (1 / act_scale)), same rounding and
  * saturation as above.  n >= 0 elements of fp32 input.

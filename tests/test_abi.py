@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -157,3 +157,25 @@ def test_quant_validation(L):
     assert f(None, B, 4, C, None) == NULL
     assert f(A + 2, B, 4, C, None) == ALIGN
     assert f(None, None, 0, None, None) == OK
+
+
+def test_rms_modulate_validation(L):
+    f = L.alnp_rms_norm_modulate_seg_bf16
+
+    def call(x=A, w=B, sc=C, sh=D, seg=B, segments=3, eps=1e-5, rows=4, dim=64, out=A, rstd=None):
+        return f(x, w, sc, sh, seg, segments, eps, rows, dim, out, rstd, None)
+    assert call(segments=0) == SHAPE
+    assert call(segments=1 << 31) == SHAPE
+    assert call(rows=-1) == SHAPE
+    assert call(dim=0) == SHAPE
+    assert call(x=None) == NULL
+    assert call(sc=None) == NULL
+    assert call(sh=None) == NULL
+    assert call(seg=None) == NULL
+    assert call(out=None) == NULL
+    assert call(w=B + 1) == ALIGN
+    assert call(seg=B + 2) == ALIGN
+    assert call(rstd=C + 2) == ALIGN
+    assert call(eps=-1.0) == ARG
+    assert call(x=None, sc=None, sh=None, seg=None, out=None, rows=0) == OK
+

@@ -1,4 +1,4 @@
-"""The entry points inside a captured HIP graph: several producers captured
+"""The entry points inside a captured HIP graph: six producers captured
 once into static output buffers, then replayed several times with eager work
 and synchronizations in between; every replay must reproduce the eager
 results byte for byte (the README's static-buffer / graph-capture usage)."""
@@ -19,6 +19,9 @@ def test_graph_replays_match_eager():
     t = inputs.make("table", rows=rows, dim=dim, seed=62)
     f = inputs.make("fp4", rows=rows, dim=dim, seed=63)
     m = inputs.make("mod6", batch=1, seq=rows, dim=dim, seed=64)
+    r = inputs.make("rmsmod", rows=rows, dim=dim, seed=66)
+    rx, rw, rsc, rsh = (dev_bf16(r[k]) for k in ("x", "weight", "scale", "shift"))
+    rseg = torch.from_numpy(r["seg"]).cuda()
     x, sc, sh = dev_bf16(p["x"]), dev_bf16(p["scale"]), dev_bf16(p["shift"])
     tx, te, tb = dev_bf16(t["x"]), dev_bf16(t["temb"]), dev_f32(t["table"])
     fx = dev_bf16(f["x"])
@@ -32,6 +35,7 @@ def test_graph_replays_match_eager():
     o_sf = torch.empty((alnp.swizzled_sf_size(rows, dim),), dtype=torch.uint8, device="cuda")
     o_m6 = [torch.empty((1, rows, dim), dtype=torch.bfloat16, device="cuda") for _ in range(6)]
     o_res = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
+    o_rms = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
     res = dev_bf16(inputs.normal_bf16((rows, dim), 1.0, 65, 1))
     proj = dev_bf16(inputs.normal_bf16((rows, dim), 1.0, 65, 2))
 
@@ -41,6 +45,7 @@ def test_graph_replays_match_eager():
         alnp.layer_norm_no_affine_quant_nvfp4_swizzled_bf16(fx, packed=o_pk, sf_swizzled=o_sf)
         alnp.adaln_modulation6_bf16(mp, mm, out=o_m6)
         alnp.gated_residual_bf16(res, o_m6[2][0], proj, out=o_res)
+        alnp.rms_norm_modulate_seg_bf16(rx, rw, rsc, rsh, rseg, out=o_rms)
 
     def scribble():
         # Fixed patterns over every output.  Bytes a producer does not own
@@ -49,14 +54,14 @@ def test_graph_replays_match_eager():
             o.view(torch.uint8).fill_(0x55)
         o_pk.fill_(0x77)
         o_sf.fill_(0x33)
-        for o in o_m6 + [o_res]:
+        for o in o_m6 + [o_res, o_rms]:
             o.view(torch.int16).fill_(-1)
         torch.cuda.synchronize()
 
     def snapshot():
         torch.cuda.synchronize()
         return [host_u8(o_ptok), host_u8(o_tab), host_u8(o_pk), host_u8(o_sf)] + \
-               [host_u16(o) for o in o_m6] + [host_u16(o_res)]
+               [host_u16(o) for o in o_m6] + [host_u16(o_res), host_u16(o_rms)]
 
     scribble()
     run_all()
