@@ -45,6 +45,7 @@ _SIGS = {
     "orc_adaln_fp8_modfp8": [_P, _P, _P, _F, _F, _F, _F, _I64, _I64, _P, _P, _P, _P],
     "orc_awq_adaln_fp8": [_P, _P, _P, _P, _F, _F, _I64, _I64, _P, _P, _P, _P],
     "orc_adaln_fp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
+    "orc_adaln_fp4_modfp8": [_P, _P, _P, _F, _F, _F, _I64, _I64, _P, _P, _P, _P, _P],
     "orc_sf_swizzle": [_P, _I64, _I64, _P],
     "orc_gated_residual": [_P, _P, _P, _I64, _I64, _I64, _P],
     "orc_bf16_modulate_n": [_P, _P, _P, _I64, _P],
@@ -351,6 +352,32 @@ def adaln_fp4(x, scale, shift, eps=1e-5, want_b=False, threads=1):
         lib().orc_adaln_fp4(_rowptr(x, r0, dim), _ptr(scale), _ptr(shift), eps, r1 - r0, dim,
                             _rowptr(packed, r0, dim // 2), _rowptr(sf, r0, dim // 16),
                             _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1), _rowptr(b, r0, dim))
+    _parallel(rows, threads, run)
+    return packed, sf, mean, rstd, b
+
+
+def adaln_fp4_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, eps=1e-5, want_b=False,
+                     threads=1):
+    """modfp8 operands (e4m3 (dim,) codes times fp32 scalars) -> AdaLN -> bf16
+    stage -> e2m1 packed + e4m3 block scales (row-major).  Returns (packed, sf,
+    mean, rstd, b)."""
+    x = _c(x, np.uint16)
+    scale_fp8 = _c(scale_fp8, np.uint8)
+    shift_fp8 = _c(shift_fp8, np.uint8)
+    rows, dim = x.shape
+    assert dim % 16 == 0 and scale_fp8.shape == shift_fp8.shape == (dim,)
+    packed = np.empty((rows, dim // 2), np.uint8)
+    sf = np.empty((rows, dim // 16), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    b = np.empty((rows, dim), np.float32) if want_b else None
+
+    def run(r0, r1):
+        lib().orc_adaln_fp4_modfp8(_rowptr(x, r0, dim), _ptr(scale_fp8), _ptr(shift_fp8),
+                                   scale_deq, shift_deq, eps, r1 - r0, dim,
+                                   _rowptr(packed, r0, dim // 2), _rowptr(sf, r0, dim // 16),
+                                   _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1),
+                                   _rowptr(b, r0, dim))
     _parallel(rows, threads, run)
     return packed, sf, mean, rstd, b
 

@@ -499,10 +499,11 @@ void orc_ln_fp4(const uint16_t* x, float eps, int64_t rows, int64_t dim,
 }
 
 /* AdaLN -> FP4 (R11): fp32 modulation, then bf16 stage and block quant. */
-void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
-                   const uint16_t* shift, float eps, int64_t rows, int64_t dim,
-                   uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
-                   float* b)
+/* AdaLN -> FP4 with fp32 modulation operands (R11): the FP8 path's fp32
+ * modulation, then the bf16 stage and the block quantization. */
+static void adaln_fp4_f32ops(const uint16_t* x, const float* sc, const float* sh, float eps,
+                             int64_t rows, int64_t dim, uint8_t* packed, uint8_t* sf,
+                             float* mean, float* rstd, float* b)
 {
     float* staged = (float*)malloc((size_t)dim * sizeof(float));
     uint8_t* codes = (uint8_t*)malloc((size_t)dim);
@@ -517,9 +518,9 @@ void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
         for (int64_t j = 0; j < dim; ++j) {
             float centered = orc_bf16_to_f32(xr[j]) - mu;
             float xhat = centered * rs;
-            float t = 1.0f + orc_bf16_to_f32(scale[j]);
+            float t = 1.0f + sc[j];
             float u = xhat * t;
-            float yj = u + orc_bf16_to_f32(shift[j]);
+            float yj = u + sh[j];
             staged[j] = orc_bf16_to_f32(orc_f32_to_bf16(yj));
             if (b)
                 b[r * dim + j] = staged[j];
@@ -531,6 +532,41 @@ void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
     }
     free(staged);
     free(codes);
+}
+
+/* Broadcast bf16 operands (exact in fp32). */
+void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
+                   const uint16_t* shift, float eps, int64_t rows, int64_t dim,
+                   uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
+                   float* b)
+{
+    float* sc = (float*)malloc((size_t)dim * sizeof(float));
+    float* sh = (float*)malloc((size_t)dim * sizeof(float));
+    for (int64_t j = 0; j < dim; ++j) {
+        sc[j] = orc_bf16_to_f32(scale[j]);
+        sh[j] = orc_bf16_to_f32(shift[j]);
+    }
+    adaln_fp4_f32ops(x, sc, sh, eps, rows, dim, packed, sf, mean, rstd, b);
+    free(sc);
+    free(sh);
+}
+
+/* modfp8 operands (R9) on the AdaLN -> FP4 path (R11): e4m3 value times its
+ * dequantization scalar, one fp32 multiplication. */
+void orc_adaln_fp4_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
+                          const uint8_t* shift_fp8, float scale_deq, float shift_deq,
+                          float eps, int64_t rows, int64_t dim, uint8_t* packed,
+                          uint8_t* sf, float* mean, float* rstd, float* b)
+{
+    float* sc = (float*)malloc((size_t)dim * sizeof(float));
+    float* sh = (float*)malloc((size_t)dim * sizeof(float));
+    for (int64_t j = 0; j < dim; ++j) {
+        sc[j] = (float)orc_e4m3_decode(scale_fp8[j]) * scale_deq;
+        sh[j] = (float)orc_e4m3_decode(shift_fp8[j]) * shift_deq;
+    }
+    adaln_fp4_f32ops(x, sc, sh, eps, rows, dim, packed, sf, mean, rstd, b);
+    free(sc);
+    free(sh);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -113,6 +113,12 @@ void orc_adaln_fp4(const uint16_t* x, const uint16_t* scale,
                    const uint16_t* shift, float eps, int64_t rows, int64_t dim,
                    uint8_t* packed, uint8_t* sf, float* mean, float* rstd,
                    float* b);
+/* ada_layer_norm_quant_nvfp4_swizzled_modfp8 arithmetic with row-major scales:
+ * operands e4m3(code) * deq (R9), then as orc_adaln_fp4. */
+void orc_adaln_fp4_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
+                          const uint8_t* shift_fp8, float scale_deq, float shift_deq,
+                          float eps, int64_t rows, int64_t dim, uint8_t* packed,
+                          uint8_t* sf, float* mean, float* rstd, float* b);
 
 /* 128x4 tiled ("swizzled") block-scale layout -- parity unpinned: the pages
  * name the layout but do not define it; this is the tiled layout NVIDIA

@@ -120,6 +120,52 @@ def test_adaln_fp4_staging_is_bf16_of_fp8_path_y(orc):
     assert np.array_equal(b, torch.from_numpy(y).to(torch.bfloat16).float().numpy())
 
 
+# ---- AdaLN -> FP4 with modfp8 operands ------------------------------------------------
+
+def test_adaln_fp4_modfp8_unit_dequant_equals_broadcast(orc):
+    """With unit dequantization scalars the modfp8 FP4 form is the broadcast
+    FP4 form fed torch's decoding of the e4m3 operands (exact in bf16)."""
+    d = inputs.make("fp4", rows=14, dim=1024, seed=29)
+    sc8 = e4m3_bits(inputs.normal_f32((1024,), 0.3, 29, 9))
+    sh8 = e4m3_bits(inputs.normal_f32((1024,), 0.3, 29, 10))
+    a = orc.adaln_fp4_modfp8(d["x"], sc8, sh8, 1.0, 1.0, want_b=True)
+    b = orc.adaln_fp4(d["x"], bf16(e4m3_vals(sc8)), bf16(e4m3_vals(sh8)), want_b=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_adaln_fp4_modfp8_dequant_scalars(orc):
+    """Power-of-two scalars scale each operand exactly and only its own; scale
+    code -1 (0xB8) leaves y = shift * shift_deq, whose block quantization the
+    codes then are."""
+    rows, dim = 5, 512
+    d = inputs.make("fp4", rows=rows, dim=dim, seed=30)
+    sc8 = e4m3_bits(inputs.normal_f32((dim,), 0.2, 30, 9))
+    sh8 = e4m3_bits(inputs.normal_f32((dim,), 0.2, 30, 10))
+    a = orc.adaln_fp4_modfp8(d["x"], sc8, sh8, 0.5, 4.0, want_b=True)
+    b = orc.adaln_fp4(d["x"], bf16(e4m3_vals(sc8) * 0.5), bf16(e4m3_vals(sh8) * 4.0), want_b=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    minus1 = np.full(dim, 0xB8, np.uint8)
+    # No +-0 shift codes: xhat * 0 + (-0) takes the sign of xhat, row by row.
+    sh8 = np.where((sh8 & 0x7F) == 0, np.uint8(0x38), sh8)
+    packed, sf, _, _, bb = orc.adaln_fp4_modfp8(d["x"], minus1, sh8, 1.0, 4.0, want_b=True)
+    shf = e4m3_vals(sh8) * np.float32(4.0)
+    assert np.array_equal(bb, np.broadcast_to(shf, bb.shape))
+    codes, scales = orc.fp4_block_quant(shf)
+    for r in range(rows):
+        assert np.array_equal(packed[r], orc.fp4_pack(codes)) and np.array_equal(sf[r], scales)
+
+
+def test_adaln_fp4_modfp8_staging_is_bf16_of_fp8_modfp8_y(orc):
+    d = inputs.make("fp4", rows=8, dim=512, seed=31)
+    sc8 = e4m3_bits(inputs.normal_f32((512,), 0.3, 31, 9))
+    sh8 = e4m3_bits(inputs.normal_f32((512,), 0.3, 31, 10))
+    _, _, _, _, b = orc.adaln_fp4_modfp8(d["x"], sc8, sh8, 0.75, 1.5, want_b=True)
+    _, _, _, y = orc.adaln_fp8_modfp8(d["x"], sc8, sh8, 0.75, 1.5, 1.0, want_y=True)
+    assert np.array_equal(b, torch.from_numpy(y).to(torch.bfloat16).float().numpy())
+
+
 # ---- swizzled scale layout (parity unpinned: properties only) ---------------------
 
 def test_swizzle_is_a_bijection_onto_the_padded_buffer(orc):
