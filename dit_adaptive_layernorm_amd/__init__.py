@@ -54,6 +54,8 @@ SIGNATURES = {
     "alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16": (
         [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_swizzled_sf_size": ([_I64, _I64], _I64),
+    "alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16": (
+        [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "alnp_rms_norm_modulate_seg_bf16": (
         [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P], _I),
@@ -350,6 +352,23 @@ def ada_layer_norm_quant_nvfp4_swizzled_bf16(x, scale, shift, eps=1e-5, packed=N
     return packed, sf
 
 
+def ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(x, scale_fp8, shift_fp8, scale_deq, shift_deq,
+                                                    eps=1e-5, packed=None, sf_swizzled=None,
+                                                    row_mean=None, row_rstd=None):
+    """AdaLN with e4m3 (dim,) scale/shift and fp32 device dequantization scalars
+    -> e2m1 packed + e4m3 block scales in the 128x4 tiled layout."""
+    rows, dim = _x(x)
+    packed, sf = _fp4_outputs(x, rows, dim, packed, sf_swizzled, True)
+    _check("alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16",
+           lib().alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(
+               x.data_ptr(), _dev(scale_fp8, "scale_fp8", torch.float8_e4m3fn, (dim,)),
+               _dev(shift_fp8, "shift_fp8", torch.float8_e4m3fn, (dim,)),
+               _scalar(scale_deq, "scale_deq"), _scalar(shift_deq, "shift_deq"), eps, rows, dim,
+               packed.data_ptr(), sf.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+               _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return packed, sf
+
+
 # ---- six-way modulation --------------------------------------------------------
 
 def adaln_modulation6_bf16(adaln_params, layer_modulation, out=None):
@@ -438,6 +457,7 @@ __all__ = [
     "awq_ada_layer_norm_quant_fp8_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
     "layer_norm_no_affine_quant_nvfp4_bf16", "layer_norm_no_affine_quant_nvfp4_swizzled_bf16",
     "ada_layer_norm_quant_nvfp4_bf16", "ada_layer_norm_quant_nvfp4_swizzled_bf16",
+    "ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16",
     "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "gated_residual_bf16",
     "rms_norm_modulate_seg_bf16", "quant_fp8_static_f32",
     "lib", "AlnpError", "SIGNATURES",

@@ -196,22 +196,42 @@ int alnp_awq_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* sc
 namespace {
 
 // Common tail of the FP4 producers (scale/shift null for LayerNorm only).
-int run_fp4(const uint16_t* x, const uint16_t* scale, const uint16_t* shift, bool modulated,
-            float eps, int64_t rows, int64_t dim, uint8_t* packed, uint8_t* sf, int layout,
-            float* row_mean, float* row_rstd, void* stream)
+Fp4Args fp4_args(const uint16_t* x, float eps, int64_t rows, int64_t dim, uint8_t* packed,
+                 uint8_t* sf, int layout, float* row_mean, float* row_rstd)
 {
-    if (int st = check_rows_dim(rows, dim, 16))
+    Fp4Args a{};
+    a.x = x;
+    a.eps = eps;
+    a.rows = rows;
+    a.dim = (int)dim;
+    a.packed = packed;
+    a.sf = sf;
+    a.sf_layout = layout;
+    a.row_mean = row_mean;
+    a.row_rstd = row_rstd;
+    a.form = alnp::kNone;
+    return a;
+}
+
+// Common tail of the FP4 producers: null/alignment/eps checks, choice of
+// kernel, launch.  a.form selects the operands that must be present.
+int run_fp4(Fp4Args a, void* stream)
+{
+    if (int st = check_rows_dim(a.rows, a.dim, 16))
         return st > 0 ? ALNP_OK : st;
-    if (!x || !packed || !sf || (modulated && (!scale || !shift)))
+    if (!a.x || !a.packed || !a.sf || (a.form == alnp::kBcast && (!a.scale || !a.shift)) ||
+        (a.form == alnp::kModFp8 &&
+         (!a.scale_fp8 || !a.shift_fp8 || !a.scale_deq || !a.shift_deq)))
         return ALNP_ERR_NULL;
-    if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(row_mean, 4) ||
-        !aligned(row_rstd, 4))
+    if (!aligned(a.x, 2) || !aligned(a.scale, 2) || !aligned(a.shift, 2) ||
+        !aligned(a.scale_deq, 4) || !aligned(a.shift_deq, 4) || !aligned(a.row_mean, 4) ||
+        !aligned(a.row_rstd, 4))
         return ALNP_ERR_ALIGN;
-    if (int st = check_eps(eps))
+    if (int st = check_eps(a.eps))
         return st;
-    Fp4Args a{x, scale, shift, eps, rows, (int)dim, packed, sf, layout, row_mean, row_rstd};
-    const bool fast = dim <= alnp::kMaxFastDim && aligned(x, 16) && aligned(scale, 16) &&
-                      aligned(shift, 16) && aligned(packed, 4);
+    const bool fast = a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) && aligned(a.scale, 16) &&
+                      aligned(a.shift, 16) && aligned(a.scale_fp8, 8) &&
+                      aligned(a.shift_fp8, 8) && aligned(a.packed, 4);
     return launch_status(alnp::launch_fp4(a, fast, as_stream(stream)));
 }
 
@@ -223,8 +243,8 @@ int alnp_layer_norm_no_affine_quant_nvfp4_bf16(const uint16_t* x, float eps, int
                                                int64_t dim, uint8_t* packed, uint8_t* sf,
                                                float* row_mean, float* row_rstd, void* stream)
 {
-    return run_fp4(x, nullptr, nullptr, false, eps, rows, dim, packed, sf, alnp::kSfRowMajor,
-                   row_mean, row_rstd, stream);
+    return run_fp4(fp4_args(x, eps, rows, dim, packed, sf, alnp::kSfRowMajor, row_mean, row_rstd),
+                   stream);
 }
 
 int alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16(const uint16_t* x, float eps,
@@ -233,8 +253,9 @@ int alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16(const uint16_t* x, float
                                                         float* row_mean, float* row_rstd,
                                                         void* stream)
 {
-    return run_fp4(x, nullptr, nullptr, false, eps, rows, dim, packed, sf_swizzled,
-                   alnp::kSfSwizzled, row_mean, row_rstd, stream);
+    return run_fp4(fp4_args(x, eps, rows, dim, packed, sf_swizzled, alnp::kSfSwizzled, row_mean,
+                            row_rstd),
+                   stream);
 }
 
 int alnp_ada_layer_norm_quant_nvfp4_bf16(const uint16_t* x, const uint16_t* scale,
@@ -242,8 +263,11 @@ int alnp_ada_layer_norm_quant_nvfp4_bf16(const uint16_t* x, const uint16_t* scal
                                          int64_t dim, uint8_t* packed, uint8_t* sf,
                                          float* row_mean, float* row_rstd, void* stream)
 {
-    return run_fp4(x, scale, shift, true, eps, rows, dim, packed, sf, alnp::kSfRowMajor,
-                   row_mean, row_rstd, stream);
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, sf, alnp::kSfRowMajor, row_mean, row_rstd);
+    a.form = alnp::kBcast;
+    a.scale = scale;
+    a.shift = shift;
+    return run_fp4(a, stream);
 }
 
 int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(const uint16_t* x, const uint16_t* scale,
@@ -252,8 +276,27 @@ int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(const uint16_t* x, const uint1
                                                   uint8_t* sf_swizzled, float* row_mean,
                                                   float* row_rstd, void* stream)
 {
-    return run_fp4(x, scale, shift, true, eps, rows, dim, packed, sf_swizzled,
-                   alnp::kSfSwizzled, row_mean, row_rstd, stream);
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, sf_swizzled, alnp::kSfSwizzled, row_mean,
+                         row_rstd);
+    a.form = alnp::kBcast;
+    a.scale = scale;
+    a.shift = shift;
+    return run_fp4(a, stream);
+}
+
+int alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(
+    const uint16_t* x, const uint8_t* scale_fp8, const uint8_t* shift_fp8,
+    const float* scale_deq, const float* shift_deq, float eps, int64_t rows, int64_t dim,
+    uint8_t* packed, uint8_t* sf_swizzled, float* row_mean, float* row_rstd, void* stream)
+{
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, sf_swizzled, alnp::kSfSwizzled, row_mean,
+                         row_rstd);
+    a.form = alnp::kModFp8;
+    a.scale_fp8 = scale_fp8;
+    a.shift_fp8 = shift_fp8;
+    a.scale_deq = scale_deq;
+    a.shift_deq = shift_deq;
+    return run_fp4(a, stream);
 }
 
 int64_t alnp_sf_size(int64_t rows, int64_t dim)

@@ -49,7 +49,7 @@ enum SfLayout {
 
 struct Fp4Args {
     const uint16_t* x;
-    const uint16_t* scale;   // broadcast (dim,) bf16, or null for LayerNorm only
+    const uint16_t* scale;   // broadcast form: (dim,) bf16
     const uint16_t* shift;
     float eps;
     int64_t rows;
@@ -60,6 +60,11 @@ struct Fp4Args {
     float* row_mean;
     float* row_rstd;
     float inv_dim;           // 1 / dim in fp32, set by the launcher
+    int form;                // kNone, kBcast (scale/shift) or kModFp8 (the fields below)
+    const uint8_t* scale_fp8;  // modfp8 form: e4m3 (dim,)
+    const uint8_t* shift_fp8;
+    const float* scale_deq;    // modfp8 form: device fp32 scalars
+    const float* shift_deq;
 };
 
 struct Mod6Args {
@@ -118,7 +123,8 @@ inline int64_t sf_swizzled_size(int64_t rows, int64_t cols)
 // fast: row kernel (dim % 8 == 0, dim <= kMaxFastDim, operands
 // 16-byte aligned); otherwise the workgroup-per-row kernel.
 hipError_t launch_adaln_fp8(const Fp8Args& a, int form, bool fast, hipStream_t s);
-// LayerNorm (a.scale null) or broadcast AdaLN -> FP4, row-major or tiled scales.
+// LayerNorm, broadcast AdaLN or modfp8 AdaLN (a.form) -> FP4, row-major or
+// tiled scales (the modfp8 form only with tiled scales).
 hipError_t launch_fp4(const Fp4Args& a, bool fast, hipStream_t s);
 hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
 // fast: dim % 8 == 0 and every pointer 16-byte aligned.

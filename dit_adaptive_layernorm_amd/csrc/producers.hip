@@ -382,14 +382,16 @@ struct E4m3Recip {
 };
 __device__ const E4m3Recip kE4m3Recip{};
 
-// LayerNorm (MOD = false) or broadcast AdaLN (MOD = true) -> FP4.
-template <int VPT, int WAVES, bool MOD, bool SWZ>
+// LayerNorm (FORM kNone), broadcast AdaLN (kBcast) or AdaLN with e4m3
+// operands and fp32 dequantization scalars (kModFp8) -> FP4.
+template <int VPT, int WAVES, int FORM, bool SWZ>
 __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
 {
     __shared__ float red[32];     // two sets of per-wave partials
     __shared__ float inv_s[128];  // 1 / s for every e4m3 scale code s
     constexpr int T = WAVES * 64;
-    constexpr int NM = MOD ? VPT : 1;
+    constexpr int NM = FORM == kBcast ? VPT : 1;
+    constexpr int N8 = FORM == kModFp8 ? VPT : 1;
     const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;  // even, since dim % 16 == 0
@@ -407,13 +409,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
     for (int v = 0; v < VPT; ++v)
         xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, v == VPT - 1);
     uint4 scv[NM], shv[NM];
-    if (MOD) {
+    uint2 sc8[N8], sh8[N8];
+    if (FORM == kBcast) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             scv[v] = ld_row<false>(a.scale, v * T + t, nvec, v == VPT - 1);
             shv[v] = ld_row<false>(a.shift, v * T + t, nvec, v == VPT - 1);
         }
+    } else if (FORM == kModFp8) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, v == VPT - 1);
+            sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, v == VPT - 1);
+        }
     }
+    const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
+    const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
     if (t < 128)
         inv_s[t] = recip0;
     if (T == 64)
@@ -441,10 +452,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
         if (v == VPT - 1 && !tail_ok)
             continue;
         float b[8], y[8];
-        if (MOD) {
+        if (FORM != kNone) {
             float sc[8], sh[8];
-            unpack8(scv[v], sc);
-            unpack8(shv[v], sh);
+            if (FORM == kModFp8) {
+                // Dequantize: e4m3 value times its fp32 scalar, one rounding.
+                unpack_e4m3x8(sc8[v], sc);
+                unpack_e4m3x8(sh8[v], sh);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sc[e] = sc[e] * sdeq;
+                    sh[e] = sh[e] * hdeq;
+                }
+            } else {
+                unpack8(scv[v], sc);
+                unpack8(shv[v], sh);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xhat = d[v][e] * rstd;
@@ -640,14 +662,19 @@ __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
     }
 }
 
-// One thread per 16-element block; modulation when a.scale is non-null.
+// One thread per 16-element block; modulation by a.form.
 __device__ __forceinline__ float fp4_block_y(const Fp4Args& a, const uint16_t* xr, int j,
                                              float mean, float rstd)
 {
     const float xhat = (ldbf(xr, j) - mean) * rstd;
-    if (!a.scale)
-        return xhat;
-    return (xhat * (1.0f + ldbf(a.scale, j))) + ldbf(a.shift, j);
+    if (a.form == kBcast)
+        return (xhat * (1.0f + ldbf(a.scale, j))) + ldbf(a.shift, j);
+    if (a.form == kModFp8) {
+        const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.scale_fp8[j], 0) * *a.scale_deq;
+        const float sh = __builtin_amdgcn_cvt_f32_fp8((int)a.shift_fp8[j], 0) * *a.shift_deq;
+        return (xhat * (1.0f + sc)) + sh;
+    }
+    return xhat;
 }
 
 __global__ __launch_bounds__(256) void k_fp4_block(Fp4Args a)
@@ -844,11 +871,11 @@ hipError_t launch_adaln_fp8(const Fp8Args& args, int form, bool fast, hipStream_
     return hipGetLastError();
 }
 
-template <bool MOD, bool SWZ>
+template <int FORM, bool SWZ>
 static hipError_t launch_fp4_rows(const Fp4Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid(a.rows);
-#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_fp4_rows<V, W, MOD, SWZ>), grid, dim3(W * 64), 0, s, a)
+#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_fp4_rows<V, W, FORM, SWZ>), grid, dim3(W * 64), 0, s, a)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)
 #undef ALNP_LAUNCH
     return hipGetLastError();
@@ -860,10 +887,19 @@ hipError_t launch_fp4(const Fp4Args& args, bool fast, hipStream_t s)
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
     if (rs.vpt > 0) {
-        const bool mod = a.scale != nullptr, swz = a.sf_layout == kSfSwizzled;
-        if (mod)
-            return swz ? launch_fp4_rows<true, true>(a, rs, s) : launch_fp4_rows<true, false>(a, rs, s);
-        return swz ? launch_fp4_rows<false, true>(a, rs, s) : launch_fp4_rows<false, false>(a, rs, s);
+        const bool swz = a.sf_layout == kSfSwizzled;
+        switch (a.form) {
+        case kNone:
+            return swz ? launch_fp4_rows<kNone, true>(a, rs, s) : launch_fp4_rows<kNone, false>(a, rs, s);
+        case kBcast:
+            return swz ? launch_fp4_rows<kBcast, true>(a, rs, s) : launch_fp4_rows<kBcast, false>(a, rs, s);
+        case kModFp8:
+            if (!swz)
+                return hipErrorInvalidValue;  // offered with tiled scales only
+            return launch_fp4_rows<kModFp8, true>(a, rs, s);
+        default:
+            return hipErrorInvalidValue;
+        }
     }
     const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
     hipLaunchKernelGGL(k_fp4_block, grid, dim3(256), 0, s, a);

@@ -225,6 +225,21 @@ int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(
     int64_t rows, int64_t dim, uint8_t* packed, uint8_t* sf_swizzled,
     float* row_mean, float* row_rstd, void* stream);
 
+/*
+ * AdaLN -> FP4 with e4m3 modulation operands (README "Available Functions":
+ * ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16; "Tensor Contract":
+ * scale_fp8/shift_fp8 e4m3 (dim,), scale_deq/shift_deq fp32 device scalars).
+ * The operands are e4m3(code) * deq (one fp32 multiplication each), then the
+ * broadcast AdaLN -> FP4 arithmetic above, with the block scales written in
+ * the 128x4 tiled layout (buffer of alnp_swizzled_sf_size bytes).
+ *   scale_fp8, shift_fp8  (dim,) e4m3 codes
+ *   scale_deq, shift_deq  device fp32 scalars (4-byte aligned)
+ */
+int alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(
+    const uint16_t* x, const uint8_t* scale_fp8, const uint8_t* shift_fp8,
+    const float* scale_deq, const float* shift_deq, float eps, int64_t rows, int64_t dim,
+    uint8_t* packed, uint8_t* sf_swizzled, float* row_mean, float* row_rstd, void* stream);
+
 /* Bytes of the tiled block-scale buffer (README: swizzled_sf_size):
  * ceil(rows / 128) * 128 * ceil(dim / 64) * 4.  Negative status for invalid
  * sizes. */

@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -118,6 +118,16 @@ def test_variant_validation(L):
     assert g(A, B, C + 2 - 1, 1e-5, 4, 64, B, C, None, None, None) == ALIGN
     h = L.alnp_layer_norm_no_affine_quant_nvfp4_swizzled_bf16
     assert h(A, 1e-5, 4, 64, B, None, None, None, None) == NULL
+    q = L.alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16
+
+    def call(x=A, s8=B, h8=C, sd=D, hd=D, eps=1e-5, rows=4, dim=64, pk=B, sf=C):
+        return q(x, s8, h8, sd, hd, eps, rows, dim, pk, sf, None, None, None)
+    assert call(s8=None) == NULL
+    assert call(hd=None) == NULL
+    assert call(sd=D + 2) == ALIGN
+    assert call(dim=40) == DIM
+    assert call(eps=math.nan) == ARG
+    assert call(x=None, s8=None, h8=None, sd=None, hd=None, rows=0, pk=None, sf=None) == OK
     assert L.alnp_swizzled_sf_size(4096, 3072) == 4096 * 192
     assert L.alnp_swizzled_sf_size(130, 48) == 256 * 4
     assert L.alnp_swizzled_sf_size(1, 16) == 128 * 4

@@ -224,6 +224,71 @@ def test_fp4_swizzled_layout(orc, mod, rows, dim):
     assert np.array_equal(got[pos], host_u8(sf_rm))
 
 
+# ---- AdaLN -> FP4 with modfp8 operands (tiled scales) ------------------------------
+
+def run_fp4_modfp8(d, sdeq, hdeq, x=None, sentinel=None):
+    rows, dim = d["x"].shape
+    sf = None
+    if sentinel is not None:
+        sf = torch.full((alnp.swizzled_sf_size(rows, dim),), sentinel, dtype=torch.uint8,
+                        device="cuda")
+    packed, sf = alnp.ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(
+        dev_bf16(d["x"]) if x is None else x, dev_u8_as_fp8(d["scale_fp8"]),
+        dev_u8_as_fp8(d["shift_fp8"]), scalar(sdeq), scalar(hdeq), sf_swizzled=sf)
+    return host_u8(packed), host_u8(sf)
+
+
+@pytest.mark.parametrize("rows,dim", FP4_SHAPES)
+def test_adaln_fp4_modfp8_shapes(orc, rows, dim):
+    print(f"adaln fp4 modfp8 rows={rows} dim={dim}", flush=True)
+    d = modfp8_inputs(rows, dim, seed=rows + 11 * dim)
+    gp, gs = run_fp4_modfp8(d, 0.75, 1.5, sentinel=0xA5)
+    rp, rs, _, _, _ = orc.adaln_fp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5)
+    cols = dim // 16
+    fp4_check(gp, gs[swizzled_positions(orc, rows, cols)], rp, rs, f"fp4 modfp8 {rows}x{dim}")
+    pc = -(-cols // 4) * 4
+    for r in range(rows):
+        for c in range(cols, pc):
+            assert gs[orc.sf_swizzled_offset(r, c, cols)] == 0
+    for r in range(rows, -(-rows // 128) * 128):
+        for c in range(pc):
+            assert gs[orc.sf_swizzled_offset(r, c, cols)] == 0xA5
+
+
+def test_adaln_fp4_modfp8_unit_dequant_equals_broadcast_bitwise():
+    # e4m3 values are exact in bf16: unit scalars give the broadcast entry's bytes.
+    rows, dim = 257, 3072
+    d = modfp8_inputs(rows, dim, seed=38)
+    sc = torch.from_numpy(d["scale_fp8"]).view(torch.float8_e4m3fn).float().to(torch.bfloat16).cuda()
+    sh = torch.from_numpy(d["shift_fp8"]).view(torch.float8_e4m3fn).float().to(torch.bfloat16).cuda()
+    gp, gs = run_fp4_modfp8(d, 1.0, 1.0, sentinel=0x3C)
+    # Same fill: padding rows of the tiled buffer are not written.
+    s2 = torch.full((alnp.swizzled_sf_size(rows, dim),), 0x3C, dtype=torch.uint8, device="cuda")
+    p2, s2 = alnp.ada_layer_norm_quant_nvfp4_swizzled_bf16(dev_bf16(d["x"]), sc, sh, sf_swizzled=s2)
+    assert np.array_equal(gp, host_u8(p2)) and np.array_equal(gs, host_u8(s2))
+
+
+def test_adaln_fp4_modfp8_full_size_sampled(orc):
+    rows, dim = 4096, 3072
+    d = modfp8_inputs(rows, dim, seed=39)
+    gp, gs = run_fp4_modfp8(d, 0.5, 2.0)
+    sel = sample_rows(rows, 128)
+    rp, rs, _, _, _ = orc.adaln_fp4_modfp8(np.ascontiguousarray(d["x"][sel]), d["scale_fp8"],
+                                           d["shift_fp8"], 0.5, 2.0, threads=8)
+    pos = swizzled_positions(orc, rows, dim // 16)[sel]
+    fp4_check(gp[sel], gs[pos], rp, rs, "fp4 modfp8 4096x3072")
+
+
+def test_adaln_fp4_modfp8_unaligned_fallback(orc):
+    rows, dim = 11, 3072
+    d = modfp8_inputs(rows, dim, seed=40)
+    x = misaligned_like((rows, dim), torch.bfloat16)
+    x.copy_(dev_bf16(d["x"]))
+    gp, gs = run_fp4_modfp8(d, 0.75, 1.5, x=x)
+    rp, rs, _, _, _ = orc.adaln_fp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5)
+    fp4_check(gp, gs[swizzled_positions(orc, rows, dim // 16)], rp, rs, "fp4 modfp8 unaligned")
+
+
 def test_adaln_fp4_zero_modulation_equals_ln_fp4_bitwise():
     d = inputs.make("fp4", rows=512, dim=3072, seed=35)
     x = dev_bf16(d["x"])
