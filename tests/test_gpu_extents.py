@@ -1,0 +1,110 @@
+"""Extents of the launch mapping, against the oracle through the C ABI: row
+counts past the 65535 workgroups one grid dimension holds (the row kernels
+then use a second grid dimension), and rows of 2^20 elements, which go to the
+workgroup-per-row fallback.  Rows on both sides of each boundary are checked."""
+import numpy as np
+import pytest
+import torch
+
+import dit_adaptive_layernorm_amd as alnp
+from dit_adaptive_layernorm_amd import inputs
+from parity import (act, assert_codes_close, assert_stats_close, dev_bf16, dev_f32, e2m1_ordinal,
+                    e4m3_ordinal, host_u8, host_u16, unpack_e2m1)
+
+pytestmark = pytest.mark.gpu
+
+GRID_X = 65535
+
+
+def boundary_rows(rows, per_group=1):
+    """Rows at the first grid-row boundary (in workgroups of per_group rows),
+    the first and the last rows."""
+    edge = GRID_X * per_group
+    picks = [0, 1, edge - 2, edge - 1, edge, edge + 1, rows - 2, rows - 1]
+    return np.unique([r for r in picks if 0 <= r < rows])
+
+
+@pytest.mark.parametrize("kind,rows", [("ptok", 70001), ("table", 140003), ("ln", 70001)])
+def test_fp8_rows_past_one_grid_dimension(orc, kind, rows):
+    dim = 64
+    print(f"fp8 {kind} rows={rows} dim={dim}", flush=True)
+    d = inputs.make(kind, rows=rows, dim=dim, seed=5)
+    x = dev_bf16(d["x"])
+    a = act(d["act_scale"])
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    if kind == "ptok":
+        o = alnp.ada_layer_norm_quant_fp8_ptok_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]),
+                                                    a, row_mean=mean, row_rstd=rstd)
+        sel = boundary_rows(rows)
+        ref = orc.adaln_fp8_ptok(d["x"][sel], d["scale"][sel], d["shift"][sel], d["act_scale"])
+    elif kind == "table":
+        o = alnp.ada_layer_norm_quant_fp8_ptok_table_bf16(
+            x, dev_bf16(d["temb"]), dev_f32(d["table"]), a, d["shift_idx"], d["scale_idx"],
+            row_mean=mean, row_rstd=rstd)
+        sel = boundary_rows(rows, per_group=2)
+        ref = orc.adaln_fp8_table(d["x"][sel], d["temb"][sel], d["table"], d["shift_idx"],
+                                  d["scale_idx"], d["act_scale"])
+    else:
+        o = alnp.layer_norm_no_affine_quant_fp8_static_bf16(x, a, row_mean=mean, row_rstd=rstd)
+        sel = boundary_rows(rows)
+        ref = orc.ln_fp8(d["x"][sel], d["act_scale"])
+    got = host_u8(o)
+    assert_codes_close(got[sel], ref[0], e4m3_ordinal, f"{kind} {rows} rows")
+    assert_stats_close(mean.cpu().numpy()[sel], rstd.cpu().numpy()[sel], ref[1], ref[2])
+
+
+def test_fp4_rows_past_one_grid_dimension(orc):
+    rows, dim = 70001, 64
+    d = inputs.make("fp4", rows=rows, dim=dim, seed=6)
+    packed, sf = alnp.layer_norm_no_affine_quant_nvfp4_bf16(dev_bf16(d["x"]))
+    sel = boundary_rows(rows)
+    rp, rs = orc.ln_fp4(d["x"][sel])[:2]
+    assert_codes_close(unpack_e2m1(host_u8(packed)[sel]), unpack_e2m1(rp), e2m1_ordinal, "fp4 codes")
+    assert_codes_close(host_u8(sf)[sel], rs, e4m3_ordinal, "fp4 scales")
+
+
+def test_rmsmod_rows_past_one_grid_dimension(orc):
+    rows, dim = 70001, 64
+    d = inputs.make("rmsmod", rows=rows, dim=dim, seed=7)
+    o = alnp.rms_norm_modulate_seg_bf16(dev_bf16(d["x"]), dev_bf16(d["weight"]),
+                                        dev_bf16(d["scale"]), dev_bf16(d["shift"]),
+                                        torch.from_numpy(d["seg"]).cuda())
+    sel = boundary_rows(rows)
+    ref = orc.rms_modulate_seg(d["x"][sel], d["weight"], d["scale"], d["shift"], d["seg"][sel])[0]
+    got = host_u16(o)[sel]
+    assert np.mean(got == ref) >= 0.999
+
+
+@pytest.mark.parametrize("kind", ["ptok", "ln"])
+def test_fp8_rows_of_2_pow_20(orc, kind):
+    rows, dim = 2, 1 << 20
+    d = inputs.make(kind, rows=rows, dim=dim, seed=8)
+    x = dev_bf16(d["x"])
+    a = act(d["act_scale"])
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    if kind == "ptok":
+        o = alnp.ada_layer_norm_quant_fp8_ptok_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]),
+                                                    a, row_mean=mean, row_rstd=rstd)
+        ref = orc.adaln_fp8_ptok(d["x"], d["scale"], d["shift"], d["act_scale"])
+    else:
+        o = alnp.layer_norm_no_affine_quant_fp8_static_bf16(x, a, row_mean=mean, row_rstd=rstd)
+        ref = orc.ln_fp8(d["x"], d["act_scale"])
+    assert_codes_close(host_u8(o), ref[0], e4m3_ordinal, f"{kind} 2 x 2^20")
+    assert_stats_close(mean.cpu().numpy(), rstd.cpu().numpy(), ref[1], ref[2])
+
+
+def test_fp4_and_rmsmod_rows_of_2_pow_20(orc):
+    rows, dim = 2, 1 << 20
+    f = inputs.make("fp4", rows=rows, dim=dim, seed=9)
+    packed, sf = alnp.layer_norm_no_affine_quant_nvfp4_bf16(dev_bf16(f["x"]))
+    rp, rs = orc.ln_fp4(f["x"])[:2]
+    assert_codes_close(unpack_e2m1(host_u8(packed)), unpack_e2m1(rp), e2m1_ordinal, "fp4 2^20")
+    assert_codes_close(host_u8(sf), rs, e4m3_ordinal, "fp4 scales 2^20")
+    r = inputs.make("rmsmod", rows=rows, dim=dim, seed=10)
+    o = alnp.rms_norm_modulate_seg_bf16(dev_bf16(r["x"]), dev_bf16(r["weight"]),
+                                        dev_bf16(r["scale"]), dev_bf16(r["shift"]),
+                                        torch.from_numpy(r["seg"]).cuda())
+    ref = orc.rms_modulate_seg(r["x"], r["weight"], r["scale"], r["shift"], r["seg"])[0]
+    assert np.mean(host_u16(o) == ref) >= 0.999
