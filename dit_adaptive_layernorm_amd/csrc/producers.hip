@@ -243,20 +243,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 constexpr int kTableRows = 2;     // rows per workgroup
 constexpr int kTableMaxDim = 8192; // 2 table rows * 8192 * 4 B = 64 KiB of LDS
 
-template <int VPT, int WAVES>
-__global__ __launch_bounds__(kTableRows * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
+template <int VPT, int WAVES, int R = kTableRows>
+__global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
 {
     extern __shared__ float4 tab[];   // [0, dim/4): scale row, [dim/4, dim/2): shift row
-    __shared__ float red[2][kTableRows * WAVES];
+    __shared__ float red[2][R * WAVES];
     constexpr int T = WAVES * 64;      // threads per row
-    constexpr int NT = kTableRows * T; // threads per workgroup
+    constexpr int NT = R * T;          // threads per workgroup
     const int tid = threadIdx.x;
     const int rr = tid / T, t = tid % T;
     const int dim = a.dim;
     const int nvec = dim >> 3;
     const int n4 = dim >> 2;
     const float inv = 1.0f / *a.act_scale;
-    const int64_t row = grid_row() * kTableRows + rr;
+    const int64_t row = grid_row() * R + rr;
     const bool valid = row < a.rows;
 
     // Table rows first: up to 8 float4 per thread in flight, the rest (only
