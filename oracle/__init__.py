@@ -50,9 +50,14 @@ _SIGS = {
     "orc_gated_residual": [_P, _P, _P, _I64, _I64, _I64, _P],
     "orc_bf16_modulate_n": [_P, _P, _P, _I64, _P],
     "orc_rms_modulate_seg": [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P],
+    "orc_mx_block_quant_n": [_P, _I64, ctypes.c_int, _P, _P],
+    "orc_adaln_mxfp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
+    "orc_adaln_mxfp8": [_P, _P, _P, ctypes.c_int, _F, _I64, _I64, _P, _P, _P, _P, _P],
 }
 
-_RESTYPES = {"orc_sf_swizzled_size": ([_I64, _I64], _I64),
+_RESTYPES = {"orc_e8m0_scale": ([_F, ctypes.c_int], ctypes.c_uint8),
+             "orc_e8m0_decode": ([ctypes.c_uint8], ctypes.c_double),
+             "orc_sf_swizzled_size": ([_I64, _I64], _I64),
              "orc_sf_swizzled_offset": ([_I64, _I64, _I64], _I64)}
 
 _lib = None
@@ -453,6 +458,73 @@ def rms_modulate_seg(x, weight, scale, shift, seg, eps=1e-5, want_n=False, threa
                                    _rowptr(rstd, r0, 1), _rowptr(n, r0, dim))
     _parallel(rows, threads, run)
     return out, rstd, n
+
+
+# ---- MX block formats (R15) -------------------------------------------------
+
+def e8m0_scale(amax, emax):
+    return int(lib().orc_e8m0_scale(float(amax), int(emax)))
+
+
+def e8m0_decode(code):
+    return float(lib().orc_e8m0_decode(int(code)))
+
+
+def mx_block_quant(v, fp4):
+    """Blocks of 32 fp32 values -> (element codes (n,), scale codes (n/32,))."""
+    v = _c(v, np.float32).ravel()
+    assert v.size % 32 == 0
+    codes = np.empty(v.size, np.uint8)
+    scales = np.empty(v.size // 32, np.uint8)
+    lib().orc_mx_block_quant_n(_ptr(v), v.size // 32, 1 if fp4 else 0, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def adaln_mxfp4(x, scale=None, shift=None, eps=1e-5, want_b=False, threads=1):
+    """LN (scale = shift = None) or broadcast AdaLN -> bf16 stage -> MXFP4.
+    Returns (packed (rows, dim/2), scales (rows, dim/32), mean, rstd, b)."""
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    assert dim % 32 == 0
+    sc = None if scale is None else _c(scale, np.uint16)
+    sh = None if shift is None else _c(shift, np.uint16)
+    packed = np.empty((rows, dim // 2), np.uint8)
+    scales = np.empty((rows, dim // 32), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    b = np.empty((rows, dim), np.float32) if want_b else None
+
+    def run(r0, r1):
+        lib().orc_adaln_mxfp4(_rowptr(x, r0, dim), _ptr(sc), _ptr(sh), eps, r1 - r0, dim,
+                              _rowptr(packed, r0, dim // 2), _rowptr(scales, r0, dim // 32),
+                              _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1), _rowptr(b, r0, dim))
+    _parallel(rows, threads, run)
+    return packed, scales, mean, rstd, b
+
+
+def adaln_mxfp8(x, scale=None, shift=None, eps=1e-5, want_y=False, threads=1):
+    """LN (None operands), broadcast ((dim,)) or per-token ((rows, dim)) AdaLN ->
+    MXFP8.  Returns (out (rows, dim) e4m3, scales (rows, dim/32), mean, rstd, y)."""
+    x = _c(x, np.uint16)
+    rows, dim = x.shape
+    assert dim % 32 == 0
+    sc = None if scale is None else _c(scale, np.uint16)
+    sh = None if shift is None else _c(shift, np.uint16)
+    per_token = sc is not None and sc.shape == (rows, dim)
+    out = np.empty((rows, dim), np.uint8)
+    scales = np.empty((rows, dim // 32), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    y = np.empty((rows, dim), np.float32) if want_y else None
+
+    def run(r0, r1):
+        lib().orc_adaln_mxfp8(_rowptr(x, r0, dim), _rowptr(sc, r0, dim) if per_token else _ptr(sc),
+                              _rowptr(sh, r0, dim) if per_token else _ptr(sh),
+                              1 if per_token else 0, eps, r1 - r0, dim, _rowptr(out, r0, dim),
+                              _rowptr(scales, r0, dim // 32), _rowptr(mean, r0, 1),
+                              _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, scales, mean, rstd, y
 
 
 # ---- six-way modulation ---------------------------------------------------

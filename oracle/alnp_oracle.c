@@ -58,6 +58,17 @@
  *      u = bf16(n * t), y = bf16(u + shift).  scale and shift are rows seg[r]
  *      of (segments, dim) tables; a row whose index is outside [0, segments)
  *      is all NaN (0x7FC0).
+ *  R15 MX block formats (not on the pages: the OCP Microscaling Formats (MX)
+ *      v1.0 specification, its conversion of a vector to an MX block; the
+ *      block format gfx950's scaled matrix instructions read).  32
+ *      consecutive elements of a row share an E8M0 scale X = 2^E with
+ *      E = floor(log2(amax)) - emax (emax = 2 for E2M1, 8 for E4M3), clamped
+ *      to [-127, 127] and stored as E + 127; each element is v / X rounded to
+ *      nearest even and saturated at the element format's largest normal.
+ *      amax ignores NaN like the FP4 block maximum; a block without a
+ *      non-zero value gets E = -127 (code 0), an infinite amax E = 127.
+ *      MXFP4 quantizes the bf16-staged value of R6/R11; MXFP8 the fp32 y of
+ *      R2, with no static act_scale (the block scale takes its place).
  */
 #include "alnp_oracle.h"
 
@@ -498,7 +509,6 @@ void orc_ln_fp4(const uint16_t* x, float eps, int64_t rows, int64_t dim,
     free(codes);
 }
 
-/* AdaLN -> FP4 (R11): fp32 modulation, then bf16 stage and block quant. */
 /* AdaLN -> FP4 with fp32 modulation operands (R11): the FP8 path's fp32
  * modulation, then the bf16 stage and the block quantization. */
 static void adaln_fp4_f32ops(const uint16_t* x, const float* sc, const float* sh, float eps,
@@ -688,4 +698,118 @@ void orc_rms_modulate_seg(const uint16_t* x, const uint16_t* weight, const uint1
                                         : (uint16_t)0x7FC0;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX block formats (R15).                                                    */
+/* ------------------------------------------------------------------------ */
+
+uint8_t orc_e8m0_scale(float amax, int emax)
+{
+    if (isinf(amax))
+        return 254;
+    if (!(amax > 0.0f))
+        return 0;
+    int e;
+    frexp((double)amax, &e); /* amax = m * 2^e with m in [0.5, 1): floor(log2) = e - 1 */
+    int E = (e - 1) - emax;
+    if (E < -127)
+        E = -127;
+    if (E > 127)
+        E = 127;
+    return (uint8_t)(E + 127);
+}
+
+double orc_e8m0_decode(uint8_t code)
+{
+    return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
+}
+
+void orc_mx_block_quant(const float* v, int64_t n, int fp4, uint8_t* codes,
+                        uint8_t* scale_code)
+{
+    float amax = 0.0f;
+    for (int64_t j = 0; j < n; ++j)
+        amax = fmaxf(amax, fabsf(v[j]));
+    uint8_t sc = orc_e8m0_scale(amax, fp4 ? 2 : 8);
+    *scale_code = sc;
+    int E = (int)sc - 127;
+    for (int64_t j = 0; j < n; ++j) {
+        /* Division by a power of two: exact in double; the float rounding can
+         * only touch values far below every non-zero code. */
+        float q = (float)ldexp((double)v[j], -E);
+        codes[j] = fp4 ? orc_e2m1_encode(q) : orc_e4m3_encode_sat(q);
+    }
+}
+
+void orc_mx_block_quant_n(const float* v, int64_t nblocks, int fp4, uint8_t* codes,
+                          uint8_t* scale_codes)
+{
+    for (int64_t k = 0; k < nblocks; ++k)
+        orc_mx_block_quant(v + 32 * k, 32, fp4, codes + 32 * k, scale_codes + k);
+}
+
+/* LayerNorm or broadcast AdaLN (scale/shift non-NULL) -> bf16 stage -> MXFP4. */
+void orc_adaln_mxfp4(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                     float eps, int64_t rows, int64_t dim, uint8_t* packed,
+                     uint8_t* scales, float* mean, float* rstd, float* b)
+{
+    float* staged = (float*)malloc((size_t)dim * sizeof(float));
+    uint8_t* codes = (uint8_t*)malloc((size_t)dim);
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        float mu, rs;
+        row_stats(xr, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        for (int64_t j = 0; j < dim; ++j) {
+            float centered = orc_bf16_to_f32(xr[j]) - mu;
+            float xhat = centered * rs;
+            float yj = xhat;
+            if (scale) {
+                float t = 1.0f + orc_bf16_to_f32(scale[j]);
+                float u = xhat * t;
+                yj = u + orc_bf16_to_f32(shift[j]);
+            }
+            staged[j] = orc_bf16_to_f32(orc_f32_to_bf16(yj));
+            if (b)
+                b[r * dim + j] = staged[j];
+        }
+        orc_mx_block_quant_n(staged, dim / 32, 1, codes, scales + r * (dim / 32));
+        orc_fp4_pack(codes, dim, packed + r * (dim / 2));
+    }
+    free(staged);
+    free(codes);
+}
+
+/* LayerNorm, broadcast or per-token AdaLN -> MXFP8: the fp32 y of R2. */
+void orc_adaln_mxfp8(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                     int per_token, float eps, int64_t rows, int64_t dim, uint8_t* out,
+                     uint8_t* scales, float* mean, float* rstd, float* y)
+{
+    float* yr = (float*)malloc((size_t)dim * sizeof(float));
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        const uint16_t* scr = scale ? scale + (per_token ? r * dim : 0) : 0;
+        const uint16_t* shr = shift ? shift + (per_token ? r * dim : 0) : 0;
+        float mu, rs;
+        row_stats(xr, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        for (int64_t j = 0; j < dim; ++j) {
+            float centered = orc_bf16_to_f32(xr[j]) - mu;
+            float xhat = centered * rs;
+            float t = 1.0f + (scr ? orc_bf16_to_f32(scr[j]) : 0.0f);
+            float u = xhat * t;
+            yr[j] = u + (shr ? orc_bf16_to_f32(shr[j]) : 0.0f);
+            if (y)
+                y[r * dim + j] = yr[j];
+        }
+        orc_mx_block_quant_n(yr, dim / 32, 0, out + r * dim, scales + r * (dim / 32));
+    }
+    free(yr);
 }

@@ -161,6 +161,27 @@ void orc_rms_modulate_seg(const uint16_t* x, const uint16_t* weight, const uint1
                           float eps, int64_t rows, int64_t dim, uint16_t* out,
                           float* rstd_out, uint16_t* n_out);
 
+/* ---- MX block formats (R15) ------------------------------------------------ */
+/* E8M0 code of the shared scale for a block maximum and the element format's
+ * emax (2 for E2M1, 8 for E4M3); value of a code (255 is NaN). */
+uint8_t orc_e8m0_scale(float amax, int emax);
+double  orc_e8m0_decode(uint8_t code);
+/* n values -> n element codes (e2m1 when fp4, else e4m3) and one scale code. */
+void orc_mx_block_quant(const float* v, int64_t n, int fp4, uint8_t* codes,
+                        uint8_t* scale_code);
+void orc_mx_block_quant_n(const float* v, int64_t nblocks, int fp4, uint8_t* codes,
+                          uint8_t* scale_codes);
+/* LN (scale = shift = NULL) or broadcast AdaLN -> bf16 stage -> MXFP4: packed
+ * (rows, dim/2), scales (rows, dim/32) E8M0. */
+void orc_adaln_mxfp4(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                     float eps, int64_t rows, int64_t dim, uint8_t* packed,
+                     uint8_t* scales, float* mean, float* rstd, float* b);
+/* LN, broadcast or per-token AdaLN -> MXFP8: out (rows, dim) e4m3, scales
+ * (rows, dim/32) E8M0; y (nullable) receives the fp32 values quantized. */
+void orc_adaln_mxfp8(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                     int per_token, float eps, int64_t rows, int64_t dim, uint8_t* out,
+                     uint8_t* scales, float* mean, float* rstd, float* y);
+
 #ifdef __cplusplus
 }
 #endif
