@@ -56,6 +56,13 @@ SIGNATURES = {
     "alnp_swizzled_sf_size": ([_I64, _I64], _I64),
     "alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16": (
         [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_layer_norm_no_affine_quant_mxfp8_bf16": ([_P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_mxfp8_bf16": ([_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_mxfp8_ptok_bf16": (
+        [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_layer_norm_no_affine_quant_mxfp4_bf16": ([_P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_mxfp4_bf16": ([_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_mx_scale_size": ([_I64, _I64], _I64),
     "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "alnp_rms_norm_modulate_seg_bf16": (
         [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P], _I),
@@ -369,6 +376,94 @@ def ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(x, scale_fp8, shift_fp8, sca
     return packed, sf
 
 
+# ---- MX block formats (E8M0 scale per 32 elements) --------------------------------
+
+_E8M0 = tuple(t for t in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if t is not None)
+
+
+def mx_scale_size(rows: int, dim: int) -> int:
+    """Bytes of an MX scale buffer: rows * dim // 32."""
+    n = lib().alnp_mx_scale_size(rows, dim)
+    if n < 0:
+        raise AlnpError("alnp_mx_scale_size", int(n))
+    return int(n)
+
+
+def _mx_scales(x, rows, dim, scales):
+    if dim % 32:
+        raise ValueError("dim must be a multiple of 32")
+    if scales is None:
+        scales = torch.empty((rows, dim // 32), dtype=torch.uint8, device=x.device)
+    if scales.dtype not in _E8M0:
+        raise TypeError("scales must be uint8 (E8M0 bytes)")
+    _dev(scales, "scales", scales.dtype, (rows, dim // 32))
+    return scales
+
+
+def _mxfp8(name, x, scale, shift, eps, out, scales, row_mean, row_rstd, op_shape):
+    rows, dim = _x(x)
+    scales = _mx_scales(x, rows, dim, scales)
+    out = _fp8_out(out, x)
+    ops = []
+    if op_shape is not None:
+        shp = op_shape(rows, dim)
+        ops = [_dev(scale, "scale", torch.bfloat16, shp), _dev(shift, "shift", torch.bfloat16, shp)]
+    _check(name, getattr(lib(), name)(
+        x.data_ptr(), *ops, eps, rows, dim, out.data_ptr(), scales.data_ptr(),
+        _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return out, scales
+
+
+def layer_norm_no_affine_quant_mxfp8_bf16(x, eps=1e-5, out=None, scales=None, row_mean=None,
+                                          row_rstd=None):
+    """LayerNorm (no affine) -> MXFP8: e4m3 (rows, dim) + E8M0 (rows, dim // 32)."""
+    return _mxfp8("alnp_layer_norm_no_affine_quant_mxfp8_bf16", x, None, None, eps, out, scales,
+                  row_mean, row_rstd, None)
+
+
+def ada_layer_norm_quant_mxfp8_bf16(x, scale, shift, eps=1e-5, out=None, scales=None,
+                                    row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> MXFP8; scale, shift (dim,) bf16."""
+    return _mxfp8("alnp_ada_layer_norm_quant_mxfp8_bf16", x, scale, shift, eps, out, scales,
+                  row_mean, row_rstd, lambda r, d: (d,))
+
+
+def ada_layer_norm_quant_mxfp8_ptok_bf16(x, scale, shift, eps=1e-5, out=None, scales=None,
+                                         row_mean=None, row_rstd=None):
+    """Per-token AdaLN -> MXFP8; scale, shift (rows, dim) bf16."""
+    return _mxfp8("alnp_ada_layer_norm_quant_mxfp8_ptok_bf16", x, scale, shift, eps, out, scales,
+                  row_mean, row_rstd, lambda r, d: (r, d))
+
+
+def _mxfp4(name, x, scale, shift, eps, packed, scales, row_mean, row_rstd):
+    rows, dim = _x(x)
+    scales = _mx_scales(x, rows, dim, scales)
+    if packed is None:
+        packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=x.device)
+    _dev(packed, "packed", torch.uint8, (rows, dim // 2))
+    ops = [] if scale is None else [_dev(scale, "scale", torch.bfloat16, (dim,)),
+                                    _dev(shift, "shift", torch.bfloat16, (dim,))]
+    _check(name, getattr(lib(), name)(
+        x.data_ptr(), *ops, eps, rows, dim, packed.data_ptr(), scales.data_ptr(),
+        _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return packed, scales
+
+
+def layer_norm_no_affine_quant_mxfp4_bf16(x, eps=1e-5, packed=None, scales=None, row_mean=None,
+                                          row_rstd=None):
+    """LayerNorm (no affine) -> bf16 stage -> MXFP4: packed e2m1 (rows, dim // 2)
+    + E8M0 (rows, dim // 32)."""
+    return _mxfp4("alnp_layer_norm_no_affine_quant_mxfp4_bf16", x, None, None, eps, packed,
+                  scales, row_mean, row_rstd)
+
+
+def ada_layer_norm_quant_mxfp4_bf16(x, scale, shift, eps=1e-5, packed=None, scales=None,
+                                    row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> bf16 stage -> MXFP4; scale, shift (dim,) bf16."""
+    return _mxfp4("alnp_ada_layer_norm_quant_mxfp4_bf16", x, scale, shift, eps, packed, scales,
+                  row_mean, row_rstd)
+
+
 # ---- six-way modulation --------------------------------------------------------
 
 def adaln_modulation6_bf16(adaln_params, layer_modulation, out=None):
@@ -460,5 +555,8 @@ __all__ = [
     "ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16",
     "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "gated_residual_bf16",
     "rms_norm_modulate_seg_bf16", "quant_fp8_static_f32",
+    "layer_norm_no_affine_quant_mxfp8_bf16", "ada_layer_norm_quant_mxfp8_bf16",
+    "ada_layer_norm_quant_mxfp8_ptok_bf16", "layer_norm_no_affine_quant_mxfp4_bf16",
+    "ada_layer_norm_quant_mxfp4_bf16", "mx_scale_size",
     "lib", "AlnpError", "SIGNATURES",
 ]

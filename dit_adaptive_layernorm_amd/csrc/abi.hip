@@ -80,6 +80,23 @@ int run_fp8(Fp8Args a, int form, void* stream)
     return launch_status(alnp::launch_adaln_fp8(a, form, fast, as_stream(stream)));
 }
 
+// MXFP8 producers (no act_scale; a.mx_scales receives the block scales).
+int run_mxfp8(Fp8Args a, int form, void* stream)
+{
+    if (int st = check_rows_dim(a.rows, a.dim, 32))
+        return st > 0 ? ALNP_OK : st;
+    if (!a.x || !a.out || !a.mx_scales || (form != alnp::kNone && (!a.scale || !a.shift)))
+        return ALNP_ERR_NULL;
+    if (!aligned(a.x, 2) || !aligned(a.scale, 2) || !aligned(a.shift, 2) ||
+        !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
+        return ALNP_ERR_ALIGN;
+    if (int st = check_eps(a.eps))
+        return st;
+    const bool fast = a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) && aligned(a.scale, 16) &&
+                      aligned(a.shift, 16) && aligned(a.out, 8);
+    return launch_status(alnp::launch_mxfp8(a, form, fast, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,7 +109,7 @@ const char* alnp_status_string(int status)
     case ALNP_OK: return "ok";
     case ALNP_ERR_NULL: return "a required pointer is NULL";
     case ALNP_ERR_SHAPE: return "rows/dim out of range";
-    case ALNP_ERR_DIM: return "dim must be even (FP8) or a multiple of 16 (FP4)";
+    case ALNP_ERR_DIM: return "dim must be even (FP8), a multiple of 16 (FP4) or of 32 (MX)";
     case ALNP_ERR_INDEX: return "chunk index outside [0, chunks)";
     case ALNP_ERR_ALIGN: return "pointer not aligned to its element size";
     case ALNP_ERR_LAUNCH: return "kernel launch failed";
@@ -217,7 +234,7 @@ Fp4Args fp4_args(const uint16_t* x, float eps, int64_t rows, int64_t dim, uint8_
 // kernel, launch.  a.form selects the operands that must be present.
 int run_fp4(Fp4Args a, void* stream)
 {
-    if (int st = check_rows_dim(a.rows, a.dim, 16))
+    if (int st = check_rows_dim(a.rows, a.dim, a.mx ? 32 : 16))
         return st > 0 ? ALNP_OK : st;
     if (!a.x || !a.packed || !a.sf || (a.form == alnp::kBcast && (!a.scale || !a.shift)) ||
         (a.form == alnp::kModFp8 &&
@@ -282,6 +299,70 @@ int alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16(const uint16_t* x, const uint1
     a.scale = scale;
     a.shift = shift;
     return run_fp4(a, stream);
+}
+
+int alnp_layer_norm_no_affine_quant_mxfp4_bf16(const uint16_t* x, float eps, int64_t rows,
+                                               int64_t dim, uint8_t* packed, uint8_t* scales,
+                                               float* row_mean, float* row_rstd, void* stream)
+{
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, scales, alnp::kSfRowMajor, row_mean, row_rstd);
+    a.mx = 1;
+    return run_fp4(a, stream);
+}
+
+int alnp_ada_layer_norm_quant_mxfp4_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps, int64_t rows,
+                                         int64_t dim, uint8_t* packed, uint8_t* scales,
+                                         float* row_mean, float* row_rstd, void* stream)
+{
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, scales, alnp::kSfRowMajor, row_mean, row_rstd);
+    a.mx = 1;
+    a.form = alnp::kBcast;
+    a.scale = scale;
+    a.shift = shift;
+    return run_fp4(a, stream);
+}
+
+int alnp_layer_norm_no_affine_quant_mxfp8_bf16(const uint16_t* x, float eps, int64_t rows,
+                                               int64_t dim, uint8_t* out, uint8_t* scales,
+                                               float* row_mean, float* row_rstd, void* stream)
+{
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    return run_mxfp8(a, alnp::kNone, stream);
+}
+
+int alnp_ada_layer_norm_quant_mxfp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps, int64_t rows,
+                                         int64_t dim, uint8_t* out, uint8_t* scales,
+                                         float* row_mean, float* row_rstd, void* stream)
+{
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    a.scale = scale;
+    a.shift = shift;
+    return run_mxfp8(a, alnp::kBcast, stream);
+}
+
+int alnp_ada_layer_norm_quant_mxfp8_ptok_bf16(const uint16_t* x, const uint16_t* scale,
+                                              const uint16_t* shift, float eps, int64_t rows,
+                                              int64_t dim, uint8_t* out, uint8_t* scales,
+                                              float* row_mean, float* row_rstd, void* stream)
+{
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    a.scale = scale;
+    a.shift = shift;
+    return run_mxfp8(a, alnp::kPtok, stream);
+}
+
+int64_t alnp_mx_scale_size(int64_t rows, int64_t dim)
+{
+    if (rows < 0 || rows > kMaxRows || dim <= 0 || dim > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (dim % 32 != 0)
+        return ALNP_ERR_DIM;
+    return rows * (dim / 32);
 }
 
 int alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(

@@ -244,6 +244,25 @@ __device__ __forceinline__ float subgroup_sum(float v, float* slot, int first, i
     return r;
 }
 
+// Max over the four lanes of a quad (the lanes holding one 32-element MX
+// block): quad_perm [1,0,3,2] then [2,3,0,1].
+__device__ __forceinline__ float quad_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    return fmaxf(v, dpp<0x4E>(v));
+}
+
+// Exponent E of an MX block scale 2^E (OCP Microscaling Formats v1.0):
+// floor(log2(amax)) - emax, clamped to [-127, 127]; -127 when amax is 0 and
+// 127 when it is infinite.  v_frexp_exp gives e with amax = m * 2^e, m in
+// [0.5, 1), so floor(log2(amax)) = e - 1.
+__device__ __forceinline__ int mx_scale_exp(float amax, int emax)
+{
+    const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - emax;
+    const int E = amax > 0.f ? min(max(e, -127), 127) : -127;
+    return amax == __builtin_inff() ? 127 : E;
+}
+
 // Max of a lane and its xor-1 partner (the two lanes holding one 16-element
 // FP4 block).
 __device__ __forceinline__ float pair_max(float v)

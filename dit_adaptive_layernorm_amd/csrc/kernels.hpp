@@ -39,6 +39,7 @@ struct Fp8Args {
     float* row_mean;
     float* row_rstd;
     float inv_dim;              // 1 / dim in fp32, set by the launcher
+    uint8_t* mx_scales;         // MXFP8: (rows, dim/32) E8M0 block scales; null otherwise
 };
 
 // Block-scale layouts of the FP4 producers.
@@ -61,6 +62,7 @@ struct Fp4Args {
     float* row_rstd;
     float inv_dim;           // 1 / dim in fp32, set by the launcher
     int form;                // kNone, kBcast (scale/shift) or kModFp8 (the fields below)
+    int mx;                  // 1: MXFP4, sf = (rows, dim/32) E8M0 scales (sf_layout row-major)
     const uint8_t* scale_fp8;  // modfp8 form: e4m3 (dim,)
     const uint8_t* shift_fp8;
     const float* scale_deq;    // modfp8 form: device fp32 scalars
@@ -131,6 +133,8 @@ hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
 hipError_t launch_gated_residual(const GateArgs& a, bool fast, hipStream_t s);
 hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t* out,
                             hipStream_t s);
+// MXFP8 (a.mx_scales non-null, act_scale unused): form kNone, kBcast or kPtok.
+hipError_t launch_mxfp8(const Fp8Args& a, int form, bool fast, hipStream_t s);
 // fast: as for launch_adaln_fp8 (x, out, weight and tables 16-byte aligned).
 hipError_t launch_rms_modulate(const RmsArgs& a, bool fast, hipStream_t s);
 

@@ -92,7 +92,9 @@ __device__ __forceinline__ uint2 ld_fp8x8(const uint8_t* p, int i, int nvec, boo
     return *reinterpret_cast<const uint2*>(p + 8 * i);
 }
 
-template <int VPT, int WAVES, int FORM>
+// MX: MXFP8 output, one E8M0 scale per 32 elements (the four vectors of a
+// lane quad) in place of the static act_scale.
+template <int VPT, int WAVES, int FORM, bool MX = false>
 __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 {
     __shared__ float red[32];  // two sets of per-wave partials
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
     const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;
-    const float inv = 1.0f / *a.act_scale;
+    const float inv = MX ? 0.f : 1.0f / *a.act_scale;
     const int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
@@ -220,7 +222,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 float y = (xhat * (1.0f + sc[e])) + sh[e];
                 if (FORM == kAwq)
                     y = y * is[e];  // per-channel smoothing before the static scale
-                q[e] = sat448(y * inv);
+                q[e] = MX ? y : sat448(y * inv);
+            }
+            if (MX) {
+                // Block scale 2^E from the quad's maximum; elements y * 2^-E
+                // (exact), saturated at 448.  The quad's lanes store the same
+                // scale byte.
+                const int E = mx_scale_exp(quad_max(absmax8(q)), 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    q[e] = sat448(__builtin_amdgcn_ldexpf(q[e], -E));
+                a.mx_scales[row * (dim >> 5) + (i >> 2)] = (uint8_t)(E + 127);
             }
             st_stream(a.out + row * dim + (int64_t)i * 8,
                       make_uint2(pack_e4m3x4(q[0], q[1], q[2], q[3]),
@@ -383,8 +395,10 @@ struct E4m3Recip {
 __device__ const E4m3Recip kE4m3Recip{};
 
 // LayerNorm (FORM kNone), broadcast AdaLN (kBcast) or AdaLN with e4m3
-// operands and fp32 dequantization scalars (kModFp8) -> FP4.
-template <int VPT, int WAVES, int FORM, bool SWZ>
+// operands and fp32 dequantization scalars (kModFp8) -> FP4: NVFP4 (e4m3
+// scale per 16 elements) or, with MX, MXFP4 (E8M0 scale per 32 elements,
+// row-major).
+template <int VPT, int WAVES, int FORM, bool SWZ, bool MX = false>
 __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
 {
     __shared__ float red[32];     // two sets of per-wave partials
@@ -401,8 +415,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
         return;  // whole workgroup
     // The encode factors 1 / s, staged from the compile-time table into LDS
     // (requested here, written once the row loads are in flight).
-    const float recip0 = t < 128 ? kE4m3Recip.v[t] : 0.f;
-    const float recip1 = T == 64 ? kE4m3Recip.v[t + 64] : 0.f;
+    const float recip0 = !MX && t < 128 ? kE4m3Recip.v[t] : 0.f;
+    const float recip1 = !MX && T == 64 ? kE4m3Recip.v[t + 64] : 0.f;
 
     uint4 xv[VPT];
 #pragma unroll
@@ -425,9 +439,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
     }
     const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
     const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
-    if (t < 128)
+    if (!MX && t < 128)
         inv_s[t] = recip0;
-    if (T == 64)
+    if (!MX && T == 64)
         inv_s[t + 64] = recip1;
 
     const bool tail_ok = (VPT - 1) * T + t < nvec;
@@ -435,7 +449,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
     row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
                    [&](float v, int k) { return group_sum(v, red + 16 * k, WAVES); }, d, mean,
                    rstd);
-    if (WAVES == 1)
+    if (WAVES == 1 && !MX)
         __syncthreads();  // inv_s visible (row_stats has no barrier for one wave)
 
     // Block scale s = e4m3(amax / 6): amax is a bf16 value, and for every
@@ -476,6 +490,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 y[e] = d[v][e] * rstd;
+        }
+        if constexpr (MX) {
+            // Stage through bf16; the block maximum of the staged values is
+            // bf16(max |y|) (rounding is monotone).  gfx950's scaled convert
+            // divides the bf16 pairs by the power-of-two scale exactly and
+            // rounds to nearest even onto E2M1 (checked for every bf16 value
+            // and every exponent).
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+            const float m = bf16_lo(pack_bf16x2(absmax8(y), 0.f));
+            const int E = mx_scale_exp(quad_max(m), 2);
+            const float xs = __uint_as_float((uint32_t)(E + 127) << 23);
+            uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[0]), xs, 0);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[1]), xs, 1);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[2]), xs, 2);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[3]), xs, 3);
+            st_stream(a.packed + row * (dim / 2) + (int64_t)i * 4, word);
+            a.sf[row * (dim >> 5) + (i >> 2)] = (uint8_t)(E + 127);
+            continue;
         }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -746,6 +781,81 @@ __global__ __launch_bounds__(256) void k_rms_mod_block(RmsArgs a)
     }
 }
 
+// MX fallbacks: one workgroup per row, one thread per 32-element block.
+__global__ __launch_bounds__(256) void k_mxfp8_block(Fp8Args a, int form)
+{
+    __shared__ float lds4[4];
+    const int dim = a.dim;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const uint16_t* xr = a.x + row * dim;
+    float mean, rstd;
+    block_row_stats(xr, dim, a.inv_dim, a.eps, lds4, mean, rstd);
+    for (int k = threadIdx.x; k < dim / 32; k += 256) {
+        float y[32];
+        float amax = 0.f;
+        for (int e = 0; e < 32; ++e) {
+            const int j = 32 * k + e;
+            float sc = 0.f, sh = 0.f;
+            if (form == kBcast) {
+                sc = ldbf(a.scale, j);
+                sh = ldbf(a.shift, j);
+            } else if (form == kPtok) {
+                sc = ldbf(a.scale, row * dim + j);
+                sh = ldbf(a.shift, row * dim + j);
+            }
+            const float xhat = (ldbf(xr, j) - mean) * rstd;
+            y[e] = (xhat * (1.0f + sc)) + sh;
+            amax = fmaxf(amax, fabsf(y[e]));
+        }
+        const int E = mx_scale_exp(amax, 8);
+        for (int e = 0; e < 32; ++e)
+            a.out[row * dim + 32 * k + e] =
+                (uint8_t)(pack_e4m3x4(sat448(__builtin_amdgcn_ldexpf(y[e], -E)), 0.f, 0.f, 0.f) & 0xFFu);
+        a.mx_scales[row * (dim / 32) + k] = (uint8_t)(E + 127);
+    }
+    if (threadIdx.x == 0) {
+        if (a.row_mean) a.row_mean[row] = mean;
+        if (a.row_rstd) a.row_rstd[row] = rstd;
+    }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_mxfp4_block(Fp4Args a)
+{
+    __shared__ float lds4[4];
+    const int dim = a.dim;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const uint16_t* xr = a.x + row * dim;
+    float mean, rstd;
+    block_row_stats(xr, dim, a.inv_dim, a.eps, lds4, mean, rstd);
+    for (int k = threadIdx.x; k < dim / 32; k += 256) {
+        uint32_t w[16];
+        float amax = 0.f;
+        for (int e = 0; e < 32; e += 2) {
+            const int j = 32 * k + e;
+            w[e / 2] = pack_bf16x2(fp4_block_y(a, xr, j, mean, rstd), fp4_block_y(a, xr, j + 1, mean, rstd));
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e / 2])), fabsf(bf16_hi(w[e / 2]))));
+        }
+        const int E = mx_scale_exp(amax, 2);
+        const float xs = __uint_as_float((uint32_t)(E + 127) << 23);
+        for (int e = 0; e < 32; e += 8) {
+            uint32_t word = 0;
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[e / 2]), xs, 0);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[e / 2 + 1]), xs, 1);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[e / 2 + 2]), xs, 2);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[e / 2 + 3]), xs, 3);
+            for (int q = 0; q < 4; ++q)
+                a.packed[row * (dim / 2) + 16 * k + e / 2 + q] = (uint8_t)(word >> (8 * q));
+        }
+        a.sf[row * (dim / 32) + k] = (uint8_t)(E + 127);
+    }
+    if (threadIdx.x == 0) {
+        if (a.row_mean) a.row_mean[row] = mean;
+        if (a.row_rstd) a.row_rstd[row] = rstd;
+    }
+    }
+}
+
 // ---- standalone quantizer ---------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_quant_fp8(const float* v, const float* act, int64_t n,
@@ -871,11 +981,42 @@ hipError_t launch_adaln_fp8(const Fp8Args& args, int form, bool fast, hipStream_
     return hipGetLastError();
 }
 
-template <int FORM, bool SWZ>
+template <int FORM>
+static hipError_t launch_mxfp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid(a.rows);
+#define ALNP_LAUNCH(V, W) \
+    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, true>), grid, dim3(W * 64), 0, s, a)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
+{
+    Fp8Args a = args;
+    a.inv_dim = 1.0f / (float)a.dim;
+    const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0) {
+        switch (form) {
+        case kNone: return launch_mxfp8_rows<kNone>(a, rs, s);
+        case kBcast: return launch_mxfp8_rows<kBcast>(a, rs, s);
+        case kPtok: return launch_mxfp8_rows<kPtok>(a, rs, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (form != kNone && form != kBcast && form != kPtok)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
+    hipLaunchKernelGGL(k_mxfp8_block, grid, dim3(256), 0, s, a, form);
+    return hipGetLastError();
+}
+
+template <int FORM, bool SWZ, bool MX = false>
 static hipError_t launch_fp4_rows(const Fp4Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid(a.rows);
-#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_fp4_rows<V, W, FORM, SWZ>), grid, dim3(W * 64), 0, s, a)
+#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_fp4_rows<V, W, FORM, SWZ, MX>), grid, dim3(W * 64), 0, s, a)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)
 #undef ALNP_LAUNCH
     return hipGetLastError();
@@ -886,6 +1027,16 @@ hipError_t launch_fp4(const Fp4Args& args, bool fast, hipStream_t s)
     Fp4Args a = args;
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (a.mx) {
+        if (a.sf_layout != kSfRowMajor || (a.form != kNone && a.form != kBcast))
+            return hipErrorInvalidValue;  // MXFP4: LN or broadcast AdaLN, row-major scales
+        if (rs.vpt > 0)
+            return a.form == kBcast ? launch_fp4_rows<kBcast, false, true>(a, rs, s)
+                                    : launch_fp4_rows<kNone, false, true>(a, rs, s);
+        const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
+        hipLaunchKernelGGL(k_mxfp4_block, grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (rs.vpt > 0) {
         const bool swz = a.sf_layout == kSfSwizzled;
         switch (a.form) {

@@ -277,6 +277,47 @@ int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
                              int64_t gate_rows, uint16_t* out, void* stream);
 
 /*
+ * MX block formats: MXFP8 (E4M3 elements) and MXFP4 (E2M1 elements, packed
+ * as above) with one E8M0 scale per 32 consecutive row elements, the operand
+ * format of gfx950's scaled matrix instructions.  The pages do not cover MX;
+ * the block rule is the OCP Microscaling Formats (MX) v1.0 specification's
+ * conversion of a vector to an MX block:
+ *   X = 2^E, E = floor(log2(amax)) - emax   (emax 8 for E4M3, 2 for E2M1),
+ *   E clamped to [-127, 127] (-127 for a block without a non-zero value,
+ *   127 for an infinite amax); scale byte = E + 127;
+ *   element = round_to_nearest_even(v / X), saturated at +-448 (E4M3) or
+ *   +-6 (E2M1); amax ignores NaN.
+ * MXFP8 quantizes the FP8 path's fp32 y (no act_scale: the block scales take
+ * its place); MXFP4 quantizes the bf16-staged value of the FP4 entries.
+ *   out      (rows, dim) e4m3 codes (MXFP8); packed (rows, dim/2) (MXFP4)
+ *   scales   (rows, dim/32) E8M0 bytes, row-major
+ * dim must be a multiple of 32 (ALNP_ERR_DIM).  Codes for NaN elements are
+ * unspecified.  Other arguments and errors as for the FP8 / FP4 entries.
+ */
+int alnp_layer_norm_no_affine_quant_mxfp8_bf16(const uint16_t* x, float eps,
+                                               int64_t rows, int64_t dim, uint8_t* out,
+                                               uint8_t* scales, float* row_mean,
+                                               float* row_rstd, void* stream);
+int alnp_ada_layer_norm_quant_mxfp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps, int64_t rows,
+                                         int64_t dim, uint8_t* out, uint8_t* scales,
+                                         float* row_mean, float* row_rstd, void* stream);
+int alnp_ada_layer_norm_quant_mxfp8_ptok_bf16(const uint16_t* x, const uint16_t* scale,
+                                              const uint16_t* shift, float eps, int64_t rows,
+                                              int64_t dim, uint8_t* out, uint8_t* scales,
+                                              float* row_mean, float* row_rstd, void* stream);
+int alnp_layer_norm_no_affine_quant_mxfp4_bf16(const uint16_t* x, float eps,
+                                               int64_t rows, int64_t dim, uint8_t* packed,
+                                               uint8_t* scales, float* row_mean,
+                                               float* row_rstd, void* stream);
+int alnp_ada_layer_norm_quant_mxfp4_bf16(const uint16_t* x, const uint16_t* scale,
+                                         const uint16_t* shift, float eps, int64_t rows,
+                                         int64_t dim, uint8_t* packed, uint8_t* scales,
+                                         float* row_mean, float* row_rstd, void* stream);
+/* Bytes of an MX scale buffer: rows * dim / 32; negative status otherwise. */
+int64_t alnp_mx_scale_size(int64_t rows, int64_t dim);
+
+/*
  * RMSNorm with segment-selected AdaLN modulation -> bf16.  Sources: the
  * RL-Kernel norm_modulate page (a modulated RMSNorm with an RMSNorm weight and
  * scale/shift rows picked per token by index_select) and the

@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 19
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -188,4 +188,25 @@ def test_rms_modulate_validation(L):
     assert call(rstd=C + 2) == ALIGN
     assert call(eps=-1.0) == ARG
     assert call(x=None, sc=None, sh=None, seg=None, out=None, rows=0) == OK
+
+
+def test_mx_validation(L):
+    f8 = L.alnp_ada_layer_norm_quant_mxfp8_ptok_bf16
+    assert f8(A, B, C, 1e-5, 4, 48, A, D, None, None, None) == DIM
+    assert f8(A, None, C, 1e-5, 4, 64, A, D, None, None, None) == NULL
+    assert f8(A, B, C, 1e-5, 4, 64, A, None, None, None, None) == NULL
+    assert f8(A + 1, B, C, 1e-5, 4, 64, A, D, None, None, None) == ALIGN
+    assert f8(A, B, C, -1.0, 4, 64, A, D, None, None, None) == ARG
+    assert f8(None, None, None, 1e-5, 0, 64, None, None, None, None, None) == OK
+    ln8 = L.alnp_layer_norm_no_affine_quant_mxfp8_bf16
+    assert ln8(A, 1e-5, 4, 64, None, D, None, None, None) == NULL
+    f4 = L.alnp_ada_layer_norm_quant_mxfp4_bf16
+    assert f4(A, B, C, 1e-5, 4, 48, B, C, None, None, None) == DIM
+    assert f4(A, None, C, 1e-5, 4, 64, B, C, None, None, None) == NULL
+    ln4 = L.alnp_layer_norm_no_affine_quant_mxfp4_bf16
+    assert ln4(A, 1e-5, 4, 64, B, None, None, None, None) == NULL
+    assert ln4(A, 1e-5, 4, 80, B, C, None, None, None) == DIM
+    assert L.alnp_mx_scale_size(4096, 3072) == 4096 * 96
+    assert L.alnp_mx_scale_size(4, 48) == DIM
+    assert alnp.mx_scale_size(2, 64) == 4
 
