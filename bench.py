@@ -71,6 +71,10 @@ def algorithmic_bytes(name, d):
         return p.nbytes + d["mod"].nbytes + p.size // 6 * 6 * 2
     x = d["x"]
     rows, dim = x.shape
+    if name.startswith("mxfp8_ptok"):
+        return 3 * x.nbytes + rows * dim + rows * dim // 32   # x, scale, shift; e4m3 + E8M0
+    if name.startswith("ln_mxfp4"):
+        return x.nbytes + rows * dim // 2 + rows * dim // 32
     if name.startswith("rmsmod"):
         # x, bf16 out, the weight, the table rows the segments use, the indices
         used = len(np.unique(d["seg"]))
@@ -114,6 +118,25 @@ class Producer:
             return
         x0 = bf(d["x"])
         rows, dim = x0.shape
+        if name.startswith("mxfp8_ptok") or name.startswith("ln_mxfp4"):
+            fp8 = name.startswith("mxfp8")
+            sc0, sh0 = (bf(d["scale"]), bf(d["shift"])) if fp8 else (None, None)
+            for _ in range(sets):
+                x = x0.clone()
+                out = torch.empty((rows, dim if fp8 else dim // 2), dtype=torch.uint8, device=dev)
+                sc_out = torch.empty((rows, dim // 32), dtype=torch.uint8, device=dev)
+                if fp8:
+                    sc, sh = sc0.clone(), sh0.clone()
+                    self.keep.append((x, sc, sh, out, sc_out))
+                    self.calls.append((self.L.alnp_ada_layer_norm_quant_mxfp8_ptok_bf16,
+                                       (x.data_ptr(), sc.data_ptr(), sh.data_ptr(), d["eps"], rows,
+                                        dim, out.data_ptr(), sc_out.data_ptr(), None, None)))
+                else:
+                    self.keep.append((x, out, sc_out))
+                    self.calls.append((self.L.alnp_layer_norm_no_affine_quant_mxfp4_bf16,
+                                       (x.data_ptr(), d["eps"], rows, dim, out.data_ptr(),
+                                        sc_out.data_ptr(), None, None)))
+            return
         if kind == "rmsmod":
             w, sc, sh = bf(d["weight"]), bf(d["scale"]), bf(d["shift"])
             seg = torch.from_numpy(d["seg"]).to(dev)
@@ -369,7 +392,8 @@ def main():
     head = "ptok_fp8_2520x3072"
     names = [head] if a.only_headline else [
         head, "table_fp8_2520x3072", "bcast_fp8_16x2048", "ln_fp8_2520x3072",
-        "ln_fp4_4096x3072", "modulation6_1x5070x3072", "rmsmod_bf16_37810x5376"]
+        "ln_fp4_4096x3072", "modulation6_1x5070x3072", "rmsmod_bf16_37810x5376",
+        "mxfp8_ptok_2520x3072", "ln_mxfp4_4096x3072"]
     if a.only:
         names = [n for n in a.only.split(",") if n]
     modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]
@@ -379,6 +403,10 @@ def main():
     for name in names:
         if name == "ln_fp8_2520x3072":
             d = inputs.make("ln", rows=2520, dim=3072)
+        elif name == "mxfp8_ptok_2520x3072":
+            d = inputs.workload("ptok_fp8_2520x3072")
+        elif name == "ln_mxfp4_4096x3072":
+            d = inputs.workload("ln_fp4_4096x3072")
         else:
             d = inputs.workload(name)
         if name == head:
