@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -327,11 +328,15 @@ PRODUCER_SOURCES = ("producers.hip", "device_common.hpp", "kernels.hpp")
 
 
 def kernel_source_hash(files=PRODUCER_SOURCES):
+    """Hash of the producer sources with comments and layout removed, so that
+    an edit to comments alone does not mark the stored counters stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "csrc")
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(f.encode() + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

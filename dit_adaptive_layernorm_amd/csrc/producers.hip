@@ -5,7 +5,11 @@
 // Contract"): LayerNorm without affine weights, DiT modulation
 // (xhat * (1 + scale)) + shift (operation order from the h3-blackwell-runtime
 // page, "NVFP4 Modulation Producer Fusion", "Exactness Contract"), then
-// static-scale e4m3 or block-16 e2m1 quantization.
+// static-scale e4m3 or block-16 e2m1 quantization.  The same row kernels
+// also write the MX block formats (E8M0 scale per 32 elements, OCP MX v1.0),
+// and a sibling kernel computes RMSNorm with segment-selected modulation in
+// bf16 operations (RL-Kernel norm_modulate page; h3 page, "Implementation
+// Phases").
 //
 // Kernel design (MI355X): the problem is a pure stream (3-7 bytes moved per
 // element, ~15 flops), so the kernels are built for HBM, not MFMA.

@@ -22,7 +22,7 @@
  *  - Errors: a negative status is returned and NOTHING is launched (outputs
  *    untouched) for: a NULL required pointer (ALNP_ERR_NULL); rows < 0,
  *    dim <= 0 or sizes past the limits below (ALNP_ERR_SHAPE); dim odd for
- *    FP8 or not a multiple of 16 for FP4 (ALNP_ERR_DIM); a chunk index
+ *    FP8, not a multiple of 16 for FP4 or of 32 for MX (ALNP_ERR_DIM); a chunk index
  *    outside [0, chunks) (ALNP_ERR_INDEX); a pointer not aligned to its
  *    element size (ALNP_ERR_ALIGN); a negative or non-finite eps
  *    (ALNP_ERR_ARG).  rows == 0 is a valid no-op.  If the launch itself
