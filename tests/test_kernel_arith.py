@@ -24,8 +24,10 @@ def test_fp4_scale_multiply_equals_division_for_every_bf16_amax(orc):
 
 
 def test_fp4_reciprocal_table_is_ieee_division(orc):
-    """The kernel tabulates 1/s per e4m3 code with the same IEEE division the
-    oracle performs per block; s values are exact in fp32."""
+    """The kernel tabulates 1/s per e4m3 code at compile time (constant
+    evaluation divides in IEEE binary32, round to nearest even), the division
+    the oracle performs per block; s values are exact in fp32.  On the GPU,
+    an input reaching every scale code checks the table against the oracle."""
     codes = np.arange(1, 127, dtype=np.uint8)
     s = orc.e4m3_decode(codes)
     assert np.array_equal(s.astype(np.float32).astype(np.float64), s)
