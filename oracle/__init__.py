@@ -53,6 +53,7 @@ _SIGS = {
     "orc_mx_block_quant_n": [_P, _I64, ctypes.c_int, _P, _P],
     "orc_adaln_mxfp4": [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P],
     "orc_adaln_mxfp8": [_P, _P, _P, ctypes.c_int, _F, _I64, _I64, _P, _P, _P, _P, _P],
+    "orc_adaln_mxfp8_table": [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _P, _P, _P, _P, _P],
 }
 
 _RESTYPES = {"orc_e8m0_scale": ([_F, ctypes.c_int], ctypes.c_uint8),
@@ -523,6 +524,30 @@ def adaln_mxfp8(x, scale=None, shift=None, eps=1e-5, want_y=False, threads=1):
                               1 if per_token else 0, eps, r1 - r0, dim, _rowptr(out, r0, dim),
                               _rowptr(scales, r0, dim // 32), _rowptr(mean, r0, 1),
                               _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
+    _parallel(rows, threads, run)
+    return out, scales, mean, rstd, y
+
+
+def adaln_mxfp8_table(x, temb, table, shift_idx, scale_idx, eps=1e-5, want_y=False, threads=1):
+    """Table form -> MXFP8.  Returns (out, scales, mean, rstd, y)."""
+    x = _c(x, np.uint16)
+    temb = _c(temb, np.uint16)
+    table = _c(table, np.float32)
+    rows, dim = x.shape
+    chunks = temb.shape[1]
+    assert dim % 32 == 0 and temb.shape == (rows, chunks, dim) and table.shape == (chunks, dim)
+    out = np.empty((rows, dim), np.uint8)
+    scales = np.empty((rows, dim // 32), np.uint8)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    y = np.empty((rows, dim), np.float32) if want_y else None
+
+    def run(r0, r1):
+        lib().orc_adaln_mxfp8_table(_rowptr(x, r0, dim), _rowptr(temb, r0, chunks * dim),
+                                    _ptr(table), chunks, shift_idx, scale_idx, eps, r1 - r0, dim,
+                                    _rowptr(out, r0, dim), _rowptr(scales, r0, dim // 32),
+                                    _rowptr(mean, r0, 1), _rowptr(rstd, r0, 1),
+                                    _rowptr(y, r0, dim))
     _parallel(rows, threads, run)
     return out, scales, mean, rstd, y
 

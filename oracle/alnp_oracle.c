@@ -813,3 +813,37 @@ void orc_adaln_mxfp8(const uint16_t* x, const uint16_t* scale, const uint16_t* s
     }
     free(yr);
 }
+
+/* Table form -> MXFP8: operands temb chunk + fp32 table row (R5), the fp32 y
+ * of R2, then MX blocks (R15). */
+void orc_adaln_mxfp8_table(const uint16_t* x, const uint16_t* temb, const float* table,
+                           int64_t chunks, int64_t shift_idx, int64_t scale_idx, float eps,
+                           int64_t rows, int64_t dim, uint8_t* out, uint8_t* scales,
+                           float* mean, float* rstd, float* y)
+{
+    float* yr = (float*)malloc((size_t)dim * sizeof(float));
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * dim;
+        float mu, rs;
+        row_stats(xr, dim, eps, &mu, &rs);
+        if (mean)
+            mean[r] = mu;
+        if (rstd)
+            rstd[r] = rs;
+        for (int64_t j = 0; j < dim; ++j) {
+            float sc = orc_bf16_to_f32(temb[(r * chunks + scale_idx) * dim + j]) +
+                       table[scale_idx * dim + j];
+            float sh = orc_bf16_to_f32(temb[(r * chunks + shift_idx) * dim + j]) +
+                       table[shift_idx * dim + j];
+            float centered = orc_bf16_to_f32(xr[j]) - mu;
+            float xhat = centered * rs;
+            float t = 1.0f + sc;
+            float u = xhat * t;
+            yr[j] = u + sh;
+            if (y)
+                y[r * dim + j] = yr[j];
+        }
+        orc_mx_block_quant_n(yr, dim / 32, 0, out + r * dim, scales + r * (dim / 32));
+    }
+    free(yr);
+}

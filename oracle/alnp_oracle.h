@@ -181,6 +181,11 @@ void orc_adaln_mxfp4(const uint16_t* x, const uint16_t* scale, const uint16_t* s
 void orc_adaln_mxfp8(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
                      int per_token, float eps, int64_t rows, int64_t dim, uint8_t* out,
                      uint8_t* scales, float* mean, float* rstd, float* y);
+/* Table form (temb (rows, chunks, dim) bf16 + table (chunks, dim) fp32) -> MXFP8. */
+void orc_adaln_mxfp8_table(const uint16_t* x, const uint16_t* temb, const float* table,
+                           int64_t chunks, int64_t shift_idx, int64_t scale_idx, float eps,
+                           int64_t rows, int64_t dim, uint8_t* out, uint8_t* scales,
+                           float* mean, float* rstd, float* y);
 
 #ifdef __cplusplus
 }

@@ -141,3 +141,15 @@ def test_mxfp8_quantizes_the_fp8_paths_y(orc):
         assert np.array_equal(y, ref_y), kind
         codes, scales = orc.mx_block_quant(y, fp4=False)
         assert np.array_equal(codes.reshape(out.shape), out) and np.array_equal(scales.reshape(s.shape), s)
+
+
+def test_mxfp8_table_quantizes_the_table_paths_y(orc):
+    d = inputs.make("table", rows=6, dim=256, seed=45)
+    out, s, _, _, y = orc.adaln_mxfp8_table(d["x"], d["temb"], d["table"], d["shift_idx"],
+                                            d["scale_idx"], want_y=True, threads=2)
+    ref_y = orc.adaln_fp8_table(d["x"], d["temb"], d["table"], d["shift_idx"], d["scale_idx"],
+                                1.0, want_y=True)[3]
+    assert np.array_equal(y, ref_y)
+    codes, scales = orc.mx_block_quant(y, fp4=False)
+    assert np.array_equal(codes.reshape(out.shape), out) and np.array_equal(scales.reshape(s.shape), s)
+
