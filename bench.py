@@ -74,6 +74,8 @@ def algorithmic_bytes(name, d):
     rows, dim = x.shape
     if name.startswith("mxfp8_ptok"):
         return 3 * x.nbytes + rows * dim + rows * dim // 32   # x, scale, shift; e4m3 + E8M0
+    if name.startswith("mxfp8_table"):
+        return 3 * x.nbytes + 2 * dim * 4 + rows * dim + rows * dim // 32  # x, 2 temb chunks, 2 table rows
     if name.startswith("ln_mxfp4"):
         return x.nbytes + rows * dim // 2 + rows * dim // 32
     if name.startswith("rmsmod"):
@@ -119,6 +121,19 @@ class Producer:
             return
         x0 = bf(d["x"])
         rows, dim = x0.shape
+        if name.startswith("mxfp8_table"):
+            te0, tb0 = bf(d["temb"]), f32(d["table"])
+            chunks = d["temb"].shape[1]
+            for _ in range(sets):
+                x, te = x0.clone(), te0.clone()
+                out = torch.empty((rows, dim), dtype=torch.uint8, device=dev)
+                sc_out = torch.empty((rows, dim // 32), dtype=torch.uint8, device=dev)
+                self.keep.append((x, te, tb0, out, sc_out))
+                self.calls.append((self.L.alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16,
+                                   (x.data_ptr(), te.data_ptr(), tb0.data_ptr(), chunks,
+                                    d["shift_idx"], d["scale_idx"], d["eps"], rows, dim,
+                                    out.data_ptr(), sc_out.data_ptr(), None, None)))
+            return
         if name.startswith("mxfp8_ptok") or name.startswith("ln_mxfp4"):
             fp8 = name.startswith("mxfp8")
             sc0, sh0 = (bf(d["scale"]), bf(d["shift"])) if fp8 else (None, None)
@@ -398,7 +413,7 @@ def main():
     names = [head] if a.only_headline else [
         head, "table_fp8_2520x3072", "bcast_fp8_16x2048", "ln_fp8_2520x3072",
         "ln_fp4_4096x3072", "modulation6_1x5070x3072", "rmsmod_bf16_37810x5376",
-        "mxfp8_ptok_2520x3072", "ln_mxfp4_4096x3072"]
+        "mxfp8_ptok_2520x3072", "mxfp8_table_2520x3072", "ln_mxfp4_4096x3072"]
     if a.only:
         names = [n for n in a.only.split(",") if n]
     modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]
@@ -410,6 +425,8 @@ def main():
             d = inputs.make("ln", rows=2520, dim=3072)
         elif name == "mxfp8_ptok_2520x3072":
             d = inputs.workload("ptok_fp8_2520x3072")
+        elif name == "mxfp8_table_2520x3072":
+            d = inputs.workload("table_fp8_2520x3072")
         elif name == "ln_mxfp4_4096x3072":
             d = inputs.workload("ln_fp4_4096x3072")
         else:

@@ -63,6 +63,8 @@ SIGNATURES = {
     "alnp_layer_norm_no_affine_quant_mxfp4_bf16": ([_P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_ada_layer_norm_quant_mxfp4_bf16": ([_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_mx_scale_size": ([_I64, _I64], _I64),
+    "alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16": (
+        [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "alnp_rms_norm_modulate_seg_bf16": (
         [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P], _I),
@@ -435,6 +437,27 @@ def ada_layer_norm_quant_mxfp8_ptok_bf16(x, scale, shift, eps=1e-5, out=None, sc
                   row_mean, row_rstd, lambda r, d: (r, d))
 
 
+def ada_layer_norm_quant_mxfp8_ptok_table_bf16(x, temb, table, shift_idx, scale_idx, eps=1e-5,
+                                               out=None, scales=None, row_mean=None,
+                                               row_rstd=None):
+    """Table-form AdaLN -> MXFP8: temb (rows, chunks, dim) bf16, table (chunks, dim)
+    fp32; operands temb[:, idx] + table[idx]."""
+    rows, dim = _x(x)
+    if temb.dim() != 3:
+        raise ValueError("temb must be (rows, chunks, dim)")
+    chunks = temb.shape[1]
+    scales = _mx_scales(x, rows, dim, scales)
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16",
+           lib().alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16(
+               x.data_ptr(), _dev(temb, "temb", torch.bfloat16, (rows, chunks, dim)),
+               _dev(table, "table", torch.float32, (chunks, dim)), chunks, int(shift_idx),
+               int(scale_idx), eps, rows, dim, out.data_ptr(), scales.data_ptr(),
+               _opt(row_mean, "row_mean", (rows,)), _opt(row_rstd, "row_rstd", (rows,)),
+               _stream()))
+    return out, scales
+
+
 def _mxfp4(name, x, scale, shift, eps, packed, scales, row_mean, row_rstd):
     rows, dim = _x(x)
     scales = _mx_scales(x, rows, dim, scales)
@@ -556,7 +579,8 @@ __all__ = [
     "sf_size", "swizzled_sf_size", "adaln_modulation6_bf16", "gated_residual_bf16",
     "rms_norm_modulate_seg_bf16", "quant_fp8_static_f32",
     "layer_norm_no_affine_quant_mxfp8_bf16", "ada_layer_norm_quant_mxfp8_bf16",
-    "ada_layer_norm_quant_mxfp8_ptok_bf16", "layer_norm_no_affine_quant_mxfp4_bf16",
+    "ada_layer_norm_quant_mxfp8_ptok_bf16", "ada_layer_norm_quant_mxfp8_ptok_table_bf16",
+    "layer_norm_no_affine_quant_mxfp4_bf16",
     "ada_layer_norm_quant_mxfp4_bf16", "mx_scale_size",
     "lib", "AlnpError", "SIGNATURES",
 ]

@@ -85,15 +85,18 @@ int run_mxfp8(Fp8Args a, int form, void* stream)
 {
     if (int st = check_rows_dim(a.rows, a.dim, 32))
         return st > 0 ? ALNP_OK : st;
-    if (!a.x || !a.out || !a.mx_scales || (form != alnp::kNone && (!a.scale || !a.shift)))
+    if (!a.x || !a.out || !a.mx_scales ||
+        ((form == alnp::kBcast || form == alnp::kPtok) && (!a.scale || !a.shift)) ||
+        (form == alnp::kTable && (!a.temb || !a.table)))
         return ALNP_ERR_NULL;
-    if (!aligned(a.x, 2) || !aligned(a.scale, 2) || !aligned(a.shift, 2) ||
-        !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
+    if (!aligned(a.x, 2) || !aligned(a.scale, 2) || !aligned(a.shift, 2) || !aligned(a.temb, 2) ||
+        !aligned(a.table, 4) || !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
         return ALNP_ERR_ALIGN;
     if (int st = check_eps(a.eps))
         return st;
     const bool fast = a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) && aligned(a.scale, 16) &&
-                      aligned(a.shift, 16) && aligned(a.out, 8);
+                      aligned(a.shift, 16) && aligned(a.temb, 16) && aligned(a.table, 16) &&
+                      aligned(a.out, 8);
     return launch_status(alnp::launch_mxfp8(a, form, fast, as_stream(stream)));
 }
 
@@ -354,6 +357,27 @@ int alnp_ada_layer_norm_quant_mxfp8_ptok_bf16(const uint16_t* x, const uint16_t*
     a.scale = scale;
     a.shift = shift;
     return run_mxfp8(a, alnp::kPtok, stream);
+}
+
+int alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16(
+    const uint16_t* x, const uint16_t* temb, const float* table, int64_t chunks, int64_t shift_idx,
+    int64_t scale_idx, float eps, int64_t rows, int64_t dim, uint8_t* out, uint8_t* scales,
+    float* row_mean, float* row_rstd, void* stream)
+{
+    if (int st = check_rows_dim(rows, dim, 32))
+        return st > 0 ? ALNP_OK : st;
+    if (chunks < 1 || chunks > kMaxDim)
+        return ALNP_ERR_SHAPE;
+    if (shift_idx < 0 || shift_idx >= chunks || scale_idx < 0 || scale_idx >= chunks)
+        return ALNP_ERR_INDEX;
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    a.temb = temb;
+    a.table = table;
+    a.chunks = chunks;
+    a.shift_idx = shift_idx;
+    a.scale_idx = scale_idx;
+    return run_mxfp8(a, alnp::kTable, stream);
 }
 
 int64_t alnp_mx_scale_size(int64_t rows, int64_t dim)

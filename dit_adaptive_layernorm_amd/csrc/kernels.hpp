@@ -133,7 +133,7 @@ hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s);
 hipError_t launch_gated_residual(const GateArgs& a, bool fast, hipStream_t s);
 hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t* out,
                             hipStream_t s);
-// MXFP8 (a.mx_scales non-null, act_scale unused): form kNone, kBcast or kPtok.
+// MXFP8 (a.mx_scales non-null, act_scale unused): form kNone, kBcast, kPtok or kTable.
 hipError_t launch_mxfp8(const Fp8Args& a, int form, bool fast, hipStream_t s);
 // fast: as for launch_adaln_fp8 (x, out, weight and tables 16-byte aligned).
 hipError_t launch_rms_modulate(const RmsArgs& a, bool fast, hipStream_t s);

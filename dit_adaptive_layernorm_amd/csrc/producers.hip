@@ -259,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 constexpr int kTableRows = 2;     // rows per workgroup
 constexpr int kTableMaxDim = 8192; // 2 table rows * 8192 * 4 B = 64 KiB of LDS
 
-template <int VPT, int WAVES, int R = kTableRows>
+template <int VPT, int WAVES, int R = kTableRows, bool MX = false>
 __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
 {
     extern __shared__ float4 tab[];   // [0, dim/4): scale row, [dim/4, dim/2): shift row
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     const int dim = a.dim;
     const int nvec = dim >> 3;
     const int n4 = dim >> 2;
-    const float inv = 1.0f / *a.act_scale;
+    const float inv = MX ? 0.f : 1.0f / *a.act_scale;
     const int64_t row = grid_row() * R + rr;
     const bool valid = row < a.rows;
 
@@ -341,7 +341,15 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
             const float shift = sh[e] + th[e];
             const float xhat = d[v][e] * rstd;
             const float y = (xhat * (1.0f + scale)) + shift;
-            q8[e] = sat448(y * inv);
+            q8[e] = MX ? y : sat448(y * inv);
+        }
+        if (MX) {
+            // MXFP8: as in k_adaln_fp8_rows (a quad of lanes holds one block).
+            const int E = mx_scale_exp(quad_max(absmax8(q8)), 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                q8[e] = sat448(__builtin_amdgcn_ldexpf(q8[e], -E));
+            a.mx_scales[row * (dim >> 5) + (i >> 2)] = (uint8_t)(E + 127);
         }
         st_stream(a.out + row * dim + (int64_t)i * 8,
                   make_uint2(pack_e4m3x4(q8[0], q8[1], q8[2], q8[3]),
@@ -806,6 +814,11 @@ __global__ __launch_bounds__(256) void k_mxfp8_block(Fp8Args a, int form)
             } else if (form == kPtok) {
                 sc = ldbf(a.scale, row * dim + j);
                 sh = ldbf(a.shift, row * dim + j);
+            } else if (form == kTable) {
+                sc = ldbf(a.temb, (row * a.chunks + a.scale_idx) * dim + j) +
+                     a.table[(int64_t)a.scale_idx * dim + j];
+                sh = ldbf(a.temb, (row * a.chunks + a.shift_idx) * dim + j) +
+                     a.table[(int64_t)a.shift_idx * dim + j];
             }
             const float xhat = (ldbf(xr, j) - mean) * rstd;
             y[e] = (xhat * (1.0f + sc)) + sh;
@@ -996,20 +1009,37 @@ static hipError_t launch_mxfp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s
     return hipGetLastError();
 }
 
+template <int V, int W>
+static void launch_table_lds_mx_shape(const Fp8Args& a, dim3 grid, size_t lds, hipStream_t s)
+{
+    if constexpr (W <= 4)
+        hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W, kTableRows, true>), grid,
+                           dim3(kTableRows * W * 64), lds, s, a);
+}
+
 hipError_t launch_mxfp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
 {
     Fp8Args a = args;
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256) {
+        const dim3 grid = row_grid((a.rows + kTableRows - 1) / kTableRows);
+        const size_t lds = 2 * (size_t)a.dim * sizeof(float);
+#define ALNP_LAUNCH(V, W) launch_table_lds_mx_shape<V, W>(a, grid, lds, s)
+        ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+        return hipGetLastError();
+    }
     if (rs.vpt > 0) {
         switch (form) {
         case kNone: return launch_mxfp8_rows<kNone>(a, rs, s);
         case kBcast: return launch_mxfp8_rows<kBcast>(a, rs, s);
         case kPtok: return launch_mxfp8_rows<kPtok>(a, rs, s);
+        case kTable: return launch_mxfp8_rows<kTable>(a, rs, s);
         default: return hipErrorInvalidValue;
         }
     }
-    if (form != kNone && form != kBcast && form != kPtok)
+    if (form != kNone && form != kBcast && form != kPtok && form != kTable)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
     hipLaunchKernelGGL(k_mxfp8_block, grid, dim3(256), 0, s, a, form);

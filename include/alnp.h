@@ -306,6 +306,12 @@ int alnp_ada_layer_norm_quant_mxfp8_ptok_bf16(const uint16_t* x, const uint16_t*
                                               const uint16_t* shift, float eps, int64_t rows,
                                               int64_t dim, uint8_t* out, uint8_t* scales,
                                               float* row_mean, float* row_rstd, void* stream);
+/* Table form: operands temb[:, idx] + table[idx] as for the FP8 table entry
+ * (chunk indices outside [0, chunks) give ALNP_ERR_INDEX). */
+int alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16(
+    const uint16_t* x, const uint16_t* temb, const float* table, int64_t chunks,
+    int64_t shift_idx, int64_t scale_idx, float eps, int64_t rows, int64_t dim, uint8_t* out,
+    uint8_t* scales, float* row_mean, float* row_rstd, void* stream);
 int alnp_layer_norm_no_affine_quant_mxfp4_bf16(const uint16_t* x, float eps,
                                                int64_t rows, int64_t dim, uint8_t* packed,
                                                uint8_t* scales, float* row_mean,

@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -206,6 +206,17 @@ def test_mx_validation(L):
     ln4 = L.alnp_layer_norm_no_affine_quant_mxfp4_bf16
     assert ln4(A, 1e-5, 4, 64, B, None, None, None, None) == NULL
     assert ln4(A, 1e-5, 4, 80, B, C, None, None, None) == DIM
+    t8 = L.alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16
+
+    def call(x=A, temb=B, table=C, chunks=6, si=0, ci=1, eps=1e-5, rows=4, dim=64, out=A, sc=D):
+        return t8(x, temb, table, chunks, si, ci, eps, rows, dim, out, sc, None, None, None)
+    assert call(si=6) == INDEX
+    assert call(chunks=0) == SHAPE
+    assert call(table=None) == NULL
+    assert call(sc=None) == NULL
+    assert call(table=C + 2) == ALIGN
+    assert call(dim=48) == DIM
+    assert call(x=None, temb=None, table=None, chunks=0, rows=0, out=None, sc=None) == OK
     assert L.alnp_mx_scale_size(4096, 3072) == 4096 * 96
     assert L.alnp_mx_scale_size(4, 48) == DIM
     assert alnp.mx_scale_size(2, 64) == 4

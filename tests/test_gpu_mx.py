@@ -1,5 +1,5 @@
 """Parity of the MX producers (MXFP8 and MXFP4, E8M0 scale per 32 elements)
-with the oracle through the C ABI: LN / broadcast / per-token forms at small
+with the oracle through the C ABI: LN / broadcast / per-token / table forms at small
 and ragged shapes (row and fallback kernels), full-size workloads on sampled
 rows, unaligned input, constant rows.
 
@@ -15,7 +15,7 @@ import torch
 
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
-from parity import dev_bf16, e2m1_ordinal, e4m3_ordinal, host_u8, misaligned_like, sample_rows, unpack_e2m1
+from parity import dev_bf16, dev_f32, e2m1_ordinal, e4m3_ordinal, host_u8, misaligned_like, sample_rows, unpack_e2m1
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,10 @@ def assert_mx_close(codes, scales, ref_codes, ref_scales, ref_values, ordinal, w
 
 def run_mxfp8(kind, d, x=None):
     x = dev_bf16(d["x"]) if x is None else x
+    if kind == "table":
+        o, s = alnp.ada_layer_norm_quant_mxfp8_ptok_table_bf16(
+            x, dev_bf16(d["temb"]), dev_f32(d["table"]), d["shift_idx"], d["scale_idx"])
+        return host_u8(o), host_u8(s)
     if kind == "ln":
         o, s = alnp.layer_norm_no_affine_quant_mxfp8_bf16(x)
     elif kind == "bcast":
@@ -50,6 +54,10 @@ def run_mxfp8(kind, d, x=None):
 
 def oracle_mxfp8(orc, kind, d, sel=None):
     pick = (lambda a: a) if sel is None else (lambda a: np.ascontiguousarray(a[sel]))
+    if kind == "table":
+        r = orc.adaln_mxfp8_table(pick(d["x"]), pick(d["temb"]), d["table"], d["shift_idx"],
+                                  d["scale_idx"], want_y=True, threads=8)
+        return r[0], r[1], r[4]
     if kind == "ln":
         r = orc.adaln_mxfp8(pick(d["x"]), want_y=True, threads=8)
     elif kind == "bcast":
@@ -81,7 +89,7 @@ SHAPES = [(1, 2048), (7, 3072), (63, 1536), (65, 1152), (9, 5376), (3, 8192), (5
           (4, 96), (2, 12000), (2, 32768), (2, 32800), (1, 40000)]
 
 
-@pytest.mark.parametrize("kind", ["ln", "bcast", "ptok"])
+@pytest.mark.parametrize("kind", ["ln", "bcast", "ptok", "table"])
 @pytest.mark.parametrize("rows,dim", SHAPES)
 def test_mxfp8_shapes(orc, kind, rows, dim):
     print(f"mxfp8 {kind} rows={rows} dim={dim}", flush=True)
@@ -101,12 +109,13 @@ def test_mxfp4_shapes(orc, kind, rows, dim):
     assert_mx_close(codes, scales, rc, rs, b, e2m1_ordinal, f"mxfp4 {kind} {rows}x{dim}")
 
 
-def test_mxfp8_full_size_sampled(orc):
-    d = inputs.workload("ptok_fp8_2520x3072")
-    codes, scales = run_mxfp8("ptok", d)
+@pytest.mark.parametrize("name,kind", [("ptok_fp8_2520x3072", "ptok"), ("table_fp8_2520x3072", "table")])
+def test_mxfp8_full_size_sampled(orc, name, kind):
+    d = inputs.workload(name)
+    codes, scales = run_mxfp8(kind, d)
     sel = sample_rows(2520, 160)
-    rc, rs, y = oracle_mxfp8(orc, "ptok", d, sel)
-    assert_mx_close(codes[sel], scales[sel], rc, rs, y, e4m3_ordinal, "mxfp8 ptok 2520x3072")
+    rc, rs, y = oracle_mxfp8(orc, kind, d, sel)
+    assert_mx_close(codes[sel], scales[sel], rc, rs, y, e4m3_ordinal, f"mxfp8 {kind} 2520x3072")
 
 
 def test_mxfp4_full_size_sampled(orc):
