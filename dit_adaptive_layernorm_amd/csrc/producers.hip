@@ -106,7 +106,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
     // Register arrays per operand kind (size 1 where the form has none).
     constexpr bool kBf16Ops = FORM == kBcast || FORM == kPtok || FORM == kTable || FORM == kAwq;
     constexpr int NB = kBf16Ops ? VPT : 1;
-    constexpr int NT = FORM == kTable ? 2 * VPT : 1;
+    // Table rows are held from the start for up to 4 vectors per thread; with
+    // more, holding them (16 floats per vector) would spill, so each vector's
+    // table values are read in the output pass instead.
+    constexpr bool kTableEarly = FORM == kTable && VPT <= 4;
+    constexpr int NT = kTableEarly ? 2 * VPT : 1;
     constexpr int N8 = FORM == kModFp8 ? VPT : 1;
     constexpr int NI = FORM == kAwq ? VPT : 1;
     const int t = threadIdx.x;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         // Table rows (fp32, shared by every row, L2-resident): also requested
         // before the reductions so their latency is not added at the end.
         float4 tsv[NT], thv[NT];
-        if (FORM == kTable) {
+        if (kTableEarly) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
                 const int i = v * T + t;
@@ -203,12 +207,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 unpack8(scv[v], sc);
                 unpack8(shv[v], sh);
                 if (FORM == kTable) {
-                    const float ts[8] = {tsv[2 * v].x, tsv[2 * v].y, tsv[2 * v].z, tsv[2 * v].w,
-                                         tsv[2 * v + 1].x, tsv[2 * v + 1].y, tsv[2 * v + 1].z,
-                                         tsv[2 * v + 1].w};
-                    const float th[8] = {thv[2 * v].x, thv[2 * v].y, thv[2 * v].z, thv[2 * v].w,
-                                         thv[2 * v + 1].x, thv[2 * v + 1].y, thv[2 * v + 1].z,
-                                         thv[2 * v + 1].w};
+                    float4 t0, t1, h0, h1;
+                    if (kTableEarly) {
+                        t0 = tsv[2 * v];
+                        t1 = tsv[2 * v + 1];
+                        h0 = thv[2 * v];
+                        h1 = thv[2 * v + 1];
+                    } else {
+                        const float4* ts = reinterpret_cast<const float4*>(a.table + (int64_t)a.scale_idx * dim + 8 * i);
+                        const float4* th = reinterpret_cast<const float4*>(a.table + (int64_t)a.shift_idx * dim + 8 * i);
+                        t0 = ts[0];
+                        t1 = ts[1];
+                        h0 = th[0];
+                        h1 = th[1];
+                    }
+                    const float ts[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+                    const float th[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         sc[e] = sc[e] + ts[e];
