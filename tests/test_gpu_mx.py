@@ -166,3 +166,18 @@ def test_mxfp8_block_scales_track_power_of_two_inputs(orc):
     codes, scales = run_mxfp8("bcast", d)
     assert np.array_equal(scales, np.broadcast_to((np.arange(-4, 4) - 8 + 127).astype(np.uint8), (rows, 8)))
     assert np.all(codes == 0x78)   # 2^k / 2^(k-8) = 256 = e4m3 0x78
+
+
+def test_batch_invariance_and_determinism():
+    # The batch-invariance page's protocol: every sub-batch reproduces the
+    # full batch's rows bit for bit, and repeated calls agree.
+    d = inputs.make("ptok", rows=1025, dim=3072, seed=46)
+    full8 = run_mxfp8("ptok", d)
+    assert all(np.array_equal(u, v) for u, v in zip(full8, run_mxfp8("ptok", d)))
+    full4 = run_mxfp4("ln", d)
+    for r0, bs in ((0, 1), (7, 33), (512, 257), (1024, 1)):
+        sub = {k: v[r0:r0 + bs] for k, v in d.items() if k in ("x", "scale", "shift")}
+        c8, s8 = run_mxfp8("ptok", sub)
+        assert np.array_equal(c8, full8[0][r0:r0 + bs]) and np.array_equal(s8, full8[1][r0:r0 + bs])
+        c4, s4 = run_mxfp4("ln", sub)
+        assert np.array_equal(c4, full4[0][r0:r0 + bs]) and np.array_equal(s4, full4[1][r0:r0 + bs])
