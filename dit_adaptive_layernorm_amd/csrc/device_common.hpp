@@ -244,6 +244,18 @@ __device__ __forceinline__ float subgroup_sum(float v, float* slot, int first, i
     return r;
 }
 
+// Clamp eight values to the e4m3 range, NaN kept (as sat448).  Scaled
+// normalized activations rarely pass 448, so one maximum over the eight
+// (NaN ignored: NaN needs no clamp) decides whether the clamps run at all.
+__device__ __forceinline__ void sat448x8(float (&v)[8])
+{
+    if (!(absmax8(v) > 448.0f))
+        return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        v[e] = sat448(v[e]);
+}
+
 // Max over the four lanes of a quad (the lanes holding one 32-element MX
 // block): quad_perm [1,0,3,2] then [2,3,0,1].
 __device__ __forceinline__ float quad_max(float v)

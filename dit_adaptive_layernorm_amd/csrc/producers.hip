@@ -240,8 +240,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 float y = (xhat * (1.0f + sc[e])) + sh[e];
                 if (FORM == kAwq)
                     y = y * is[e];  // per-channel smoothing before the static scale
-                q[e] = MX ? y : sat448(y * inv);
+                q[e] = MX ? y : y * inv;
             }
+            if (!MX)
+                sat448x8(q);
             if (MX) {
                 // Block scale 2^E from the quad's maximum; elements y * 2^-E
                 // (exact), saturated at 448.  The quad's lanes store the same
@@ -355,8 +357,10 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
             const float shift = sh[e] + th[e];
             const float xhat = d[v][e] * rstd;
             const float y = (xhat * (1.0f + scale)) + shift;
-            q8[e] = MX ? y : sat448(y * inv);
+            q8[e] = MX ? y : y * inv;
         }
+        if (!MX)
+            sat448x8(q8);
         if (MX) {
             // MXFP8: as in k_adaln_fp8_rows (a quad of lanes holds one block).
             const int E = mx_scale_exp(quad_max(absmax8(q8)), 8);
