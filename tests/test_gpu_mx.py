@@ -15,7 +15,8 @@ import torch
 
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
-from parity import dev_bf16, dev_f32, e2m1_ordinal, e4m3_ordinal, host_u8, misaligned_like, sample_rows, unpack_e2m1
+from parity import (assert_stats_close, dev_bf16, dev_f32, e2m1_ordinal, e4m3_ordinal, host_u8,
+                    misaligned_like, sample_rows, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +182,33 @@ def test_batch_invariance_and_determinism():
         assert np.array_equal(c8, full8[0][r0:r0 + bs]) and np.array_equal(s8, full8[1][r0:r0 + bs])
         c4, s4 = run_mxfp4("ln", sub)
         assert np.array_equal(c4, full4[0][r0:r0 + bs]) and np.array_equal(s4, full4[1][r0:r0 + bs])
+
+
+def test_infinite_block_maximum(orc):
+    # A huge broadcast scale overflows y (and its bf16 stage) to +-inf in some
+    # blocks: the block maximum is infinite, E = 127, infinities saturate and
+    # the finite values of the block divide by 2^127.
+    rows, dim = 3, 512
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=47)
+    d["scale"] = inputs.to_bf16_bits(np.full(dim, 3.0e38, np.float32))
+    codes, scales = run_mxfp8("bcast", d)
+    rc, rs, y = oracle_mxfp8(orc, "bcast", d)
+    assert np.any(rs == 254) and np.array_equal(scales, rs) and np.array_equal(codes, rc)
+    c4, s4 = run_mxfp4("bcast", d)
+    r4, rs4, _ = oracle_mxfp4(orc, "bcast", d)
+    assert np.any(rs4 == 254) and np.array_equal(s4, rs4) and np.array_equal(c4, r4)
+
+
+def test_row_statistics(orc):
+    rows, dim = 33, 3072
+    d = inputs.make("ptok", rows=rows, dim=dim, seed=48)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    alnp.ada_layer_norm_quant_mxfp8_ptok_bf16(dev_bf16(d["x"]), dev_bf16(d["scale"]),
+                                              dev_bf16(d["shift"]), row_mean=mean, row_rstd=rstd)
+    _, _, rm, rr, _ = orc.adaln_mxfp8(d["x"], d["scale"], d["shift"])
+    assert_stats_close(mean.cpu().numpy(), rstd.cpu().numpy(), rm, rr)
+    m4 = torch.empty_like(mean)
+    r4 = torch.empty_like(rstd)
+    alnp.layer_norm_no_affine_quant_mxfp4_bf16(dev_bf16(d["x"]), row_mean=m4, row_rstd=r4)
+    assert_stats_close(m4.cpu().numpy(), r4.cpu().numpy(), rm, rr)
