@@ -338,8 +338,8 @@ def launch_overhead(torch, alnp, inputs, stream, calls=400, graph_launches=32, r
 
 # ---- counters from rocprofv3 (profiles/) --------------------------------------------
 
-# Sources that build the row-producer kernels (the headline kernel).
-PRODUCER_SOURCES = ("producers.hip", "device_common.hpp", "kernels.hpp")
+# Sources that build the FP8 row-producer kernels (the headline kernel).
+PRODUCER_SOURCES = ("producers.hip", "rows.hpp", "device_common.hpp", "kernels.hpp")
 
 
 def kernel_source_hash(files=PRODUCER_SOURCES):

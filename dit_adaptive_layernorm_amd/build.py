@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libalnp.so")
-SOURCES = ["producers.hip", "modulation6.hip", "residual.hip", "abi.hip"]
+SOURCES = ["producers.hip", "fp4.hip", "rmsmod.hip", "modulation6.hip", "residual.hip", "abi.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -44,7 +44,7 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
+def build(verbose: bool = False, jobs: int = 6) -> str:
     with tempfile.TemporaryDirectory(prefix="alnp_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:

@@ -1,0 +1,143 @@
+// rmsmod.hip -- RMSNorm with segment-selected modulation -> bf16, for gfx950.
+//
+// RMSNorm with an optional weight, then (n * (scale[seg] + 1)) + shift[seg]
+// with every step a bf16 operation (RL-Kernel norm_modulate page; h3 page,
+// "Implementation Phases" and "NVFP4 Modulation Producer Fusion",
+// "Exactness Contract").
+#include "rows.hpp"
+
+namespace alnp {
+
+// One modulated pair: the bf16 RMSNorm outputs n of two elements (already
+// rounded, packed), their operands, and the bf16 results packed.  Each step
+// is an fp32 operation rounded to bf16: t = bf16(scale + 1), u = bf16(n * t),
+// y = bf16(u + shift).
+__device__ __forceinline__ uint32_t modulate_bf16x2(uint32_t n, float sc0, float sc1, float sh0,
+                                                    float sh1)
+{
+    const uint32_t t = pack_bf16x2(sc0 + 1.0f, sc1 + 1.0f);
+    const uint32_t u = pack_bf16x2(bf16_lo(n) * bf16_lo(t), bf16_hi(n) * bf16_hi(t));
+    return pack_bf16x2(bf16_lo(u) + sh0, bf16_hi(u) + sh1);
+}
+
+// One workgroup per row, the row in registers (same shapes as the FP8
+// kernels).  The row's table index is one uniform load; an index outside
+// [0, segments) reads table row 0 (in bounds) and writes NaN.  The sum of
+// squares is a single reduction: v_dot2_f32_bf16 of each bf16 pair with
+// itself, DPP wave sums, one LDS exchange.
+template <int VPT, int WAVES, bool W>
+__global__ __launch_bounds__(WAVES * 64) void k_rms_mod_rows(RmsArgs a)
+{
+    __shared__ float red[16];
+    constexpr int T = WAVES * 64;
+    constexpr int NW = W ? VPT : 1;
+    const int t = threadIdx.x;
+    const int dim = a.dim;
+    const int nvec = dim >> 3;
+    const int64_t row = grid_row();
+    if (row >= a.rows)
+        return;  // whole workgroup
+    const int32_t sidx = a.seg[row];
+    const bool in_range = sidx >= 0 && sidx < a.segments;
+    const int64_t srow = in_range ? sidx : 0;
+
+    uint4 xv[VPT], wv[NW], scv[VPT], shv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, v == VPT - 1);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        if (W)
+            wv[v] = ld_row<false>(a.weight, v * T + t, nvec, v == VPT - 1);
+        scv[v] = ld_row<false>(a.scale + srow * dim, v * T + t, nvec, v == VPT - 1);
+        shv[v] = ld_row<false>(a.shift + srow * dim, v * T + t, nvec, v == VPT - 1);
+    }
+    float q = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        q = sumsq_bf16x8(xv[v], q);
+    const float rstd = rsqrt_refined(group_sum(q, red, WAVES) * a.inv_dim + a.eps);
+
+    const bool tail_ok = (VPT - 1) * T + t < nvec;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * T + t;
+        if (v == VPT - 1 && !tail_ok)
+            continue;
+        float f[8], w8[8], sc[8], sh[8];
+        unpack8(xv[v], f);
+        if (W)
+            unpack8(wv[v], w8);
+        unpack8(scv[v], sc);
+        unpack8(shv[v], sh);
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float n0 = f[2 * k] * rstd, n1 = f[2 * k + 1] * rstd;
+            if (W) {
+                n0 = n0 * w8[2 * k];
+                n1 = n1 * w8[2 * k + 1];
+            }
+            o[k] = modulate_bf16x2(pack_bf16x2(n0, n1), sc[2 * k], sc[2 * k + 1], sh[2 * k],
+                                   sh[2 * k + 1]);
+            o[k] = in_range ? o[k] : 0x7FC07FC0u;
+        }
+        st_stream(a.out + row * dim + (int64_t)i * 8, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+    if (t == 0 && a.row_rstd)
+        a.row_rstd[row] = rstd;
+}
+
+__global__ __launch_bounds__(256) void k_rms_mod_block(RmsArgs a)
+{
+    __shared__ float lds4[4];
+    const int dim = a.dim;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const uint16_t* xr = a.x + row * dim;
+    const int32_t sidx = a.seg[row];
+    const bool in_range = sidx >= 0 && sidx < a.segments;
+    const int64_t srow = in_range ? sidx : 0;
+    float q = 0.f;
+    for (int j = threadIdx.x; j < dim; j += 256) {
+        const float v = ldbf(xr, j);
+        q = __builtin_fmaf(v, v, q);
+    }
+    const float rstd = rsqrt_refined(block_sum(q, lds4) * a.inv_dim + a.eps);
+    for (int j = threadIdx.x; j < dim; j += 256) {
+        float n = ldbf(xr, j) * rstd;
+        if (a.weight)
+            n = n * ldbf(a.weight, j);
+        const uint32_t y = modulate_bf16x2(pack_bf16x2(n, 0.f), ldbf(a.scale, srow * dim + j), 0.f,
+                                           ldbf(a.shift, srow * dim + j), 0.f);
+        a.out[row * dim + j] = in_range ? (uint16_t)(y & 0xFFFFu) : (uint16_t)0x7FC0;
+    }
+    if (threadIdx.x == 0 && a.row_rstd)
+        a.row_rstd[row] = rstd;
+    }
+}
+
+// ---- launchers ----------------------------------------------------------------
+
+template <bool W>
+static hipError_t launch_rms_rows(const RmsArgs& a, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid(a.rows);
+#define ALNP_LAUNCH(V, WV) hipLaunchKernelGGL((k_rms_mod_rows<V, WV, W>), grid, dim3(WV * 64), 0, s, a)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_rms_modulate(const RmsArgs& args, bool fast, hipStream_t s)
+{
+    RmsArgs a = args;
+    a.inv_dim = 1.0f / (float)a.dim;
+    const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
+    if (rs.vpt > 0)
+        return a.weight ? launch_rms_rows<true>(a, rs, s) : launch_rms_rows<false>(a, rs, s);
+    const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
+    hipLaunchKernelGGL(k_rms_mod_block, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace alnp
