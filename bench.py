@@ -57,6 +57,8 @@ def parse():
                    help="launch each step directly instead of replaying a HIP graph")
     p.add_argument("--no-overhead", action="store_true",
                    help="skip the small-shape launch-overhead table")
+    p.add_argument("--no-floor", action="store_true",
+                   help="skip timing the memory-only counterparts (libalnp_floor.so)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run four plain device copies of 256 MiB (reference for "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -94,13 +96,40 @@ def algorithmic_bytes(name, d):
     return b
 
 
+def floor_lib():
+    """libalnp_floor.so (memory-only counterparts of the producers, built with
+    libalnp.so), or None if it was not built."""
+    path = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "libalnp_floor.so")
+    if not os.path.exists(path):
+        return None
+    F = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    F.alnp_floor_rows.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    F.alnp_floor_rows.restype = ctypes.c_int
+    F.alnp_floor_modulation6.argtypes = [vp, i64, ctypes.c_int, ctypes.POINTER(vp), vp]
+    F.alnp_floor_modulation6.restype = ctypes.c_int
+    return F
+
+
+# out_kind of alnp_floor_rows
+FLOOR_FP8, FLOOR_NVFP4, FLOOR_BF16, FLOOR_MXFP8, FLOOR_MXFP4 = 0, 1, 2, 3, 4
+
+
 class Producer:
     """Device buffers for `sets` copies of one workload and a raw C-ABI
-    launcher for set i (pointers precomputed: the step is the library call)."""
+    launcher for set i (pointers precomputed: the step is the library call).
+    With a floor library, `floor_calls` holds, per set, the memory-only
+    counterpart of the call on the same buffers."""
 
-    def __init__(self, name, d, sets, torch, alnp):
+    def __init__(self, name, d, sets, torch, alnp, floor=None):
         self.name, self.d, self.sets = name, d, sets
         self.torch, self.L = torch, alnp.lib()
+        F = floor
+        self.floor_calls = [] if F is not None else None
+
+        def add_floor(fn_args):
+            if F is not None:
+                self.floor_calls.append(fn_args)
         dev = torch.device("cuda")
         bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
@@ -117,6 +146,8 @@ class Producer:
                 self.keep += [p, m, outs, arr]
                 self.calls.append((self.L.alnp_adaln_modulation6_bf16,
                                    (p.data_ptr(), m.data_ptr(), B, S, D, arr)))
+                if F is not None:
+                    add_floor((F.alnp_floor_modulation6, (p.data_ptr(), B * S, D, arr)))
             self.outs = lambda i: self.keep[4 * i + 2]
             return
         x0 = bf(d["x"])
@@ -133,6 +164,11 @@ class Producer:
                                    (x.data_ptr(), te.data_ptr(), tb0.data_ptr(), chunks,
                                     d["shift_idx"], d["scale_idx"], d["eps"], rows, dim,
                                     out.data_ptr(), sc_out.data_ptr(), None, None)))
+                if F is not None:
+                    add_floor((F.alnp_floor_rows,
+                               (x.data_ptr(), te.data_ptr() + 2 * int(d["scale_idx"]) * dim,
+                                te.data_ptr() + 2 * int(d["shift_idx"]) * dim, chunks * dim, rows,
+                                dim, FLOOR_MXFP8, out.data_ptr(), sc_out.data_ptr())))
             return
         if name.startswith("mxfp8_ptok") or name.startswith("ln_mxfp4"):
             fp8 = name.startswith("mxfp8")
@@ -147,11 +183,19 @@ class Producer:
                     self.calls.append((self.L.alnp_ada_layer_norm_quant_mxfp8_ptok_bf16,
                                        (x.data_ptr(), sc.data_ptr(), sh.data_ptr(), d["eps"], rows,
                                         dim, out.data_ptr(), sc_out.data_ptr(), None, None)))
+                    if F is not None:
+                        add_floor((F.alnp_floor_rows,
+                                   (x.data_ptr(), sc.data_ptr(), sh.data_ptr(), dim, rows, dim,
+                                    FLOOR_MXFP8, out.data_ptr(), sc_out.data_ptr())))
                 else:
                     self.keep.append((x, out, sc_out))
                     self.calls.append((self.L.alnp_layer_norm_no_affine_quant_mxfp4_bf16,
                                        (x.data_ptr(), d["eps"], rows, dim, out.data_ptr(),
                                         sc_out.data_ptr(), None, None)))
+                    if F is not None:
+                        add_floor((F.alnp_floor_rows,
+                                   (x.data_ptr(), None, None, 0, rows, dim, FLOOR_MXFP4,
+                                    out.data_ptr(), sc_out.data_ptr())))
             return
         if kind == "rmsmod":
             w, sc, sh = bf(d["weight"]), bf(d["scale"]), bf(d["shift"])
@@ -164,6 +208,9 @@ class Producer:
                                    (x.data_ptr(), w.data_ptr(), sc.data_ptr(), sh.data_ptr(),
                                     seg.data_ptr(), sc.shape[0], d["eps"], rows, dim,
                                     out.data_ptr(), None)))
+                if F is not None:
+                    add_floor((F.alnp_floor_rows, (x.data_ptr(), None, None, 0, rows, dim,
+                                                   FLOOR_BF16, out.data_ptr(), None)))
             return
         act0 = torch.tensor([d.get("act_scale", 0.025)], dtype=torch.float32, device=dev)
         ops = {}
@@ -181,9 +228,26 @@ class Producer:
                 self.calls.append((self.L.alnp_layer_norm_no_affine_quant_nvfp4_bf16,
                                    (x.data_ptr(), d["eps"], rows, dim, packed.data_ptr(),
                                     sf.data_ptr(), None, None)))
+                if F is not None:
+                    add_floor((F.alnp_floor_rows, (x.data_ptr(), None, None, 0, rows, dim,
+                                                   FLOOR_NVFP4, packed.data_ptr(), sf.data_ptr())))
                 continue
             out = torch.empty((rows, dim), dtype=torch.uint8, device=dev)
             self.keep.append((x, act, o, out))
+            if F is not None:
+                if kind == "ln":
+                    a_ptr = b_ptr = None
+                    stride = 0
+                elif kind in ("bcast", "ptok"):
+                    a_ptr, b_ptr = o["scale"].data_ptr(), o["shift"].data_ptr()
+                    stride = dim if kind == "ptok" else 0
+                else:
+                    chunks = d["temb"].shape[1]
+                    a_ptr = o["temb"].data_ptr() + 2 * int(d["scale_idx"]) * dim
+                    b_ptr = o["temb"].data_ptr() + 2 * int(d["shift_idx"]) * dim
+                    stride = chunks * dim
+                add_floor((F.alnp_floor_rows, (x.data_ptr(), a_ptr, b_ptr, stride, rows, dim,
+                                               FLOOR_FP8, out.data_ptr(), None)))
             if kind == "ln":
                 self.calls.append((self.L.alnp_layer_norm_no_affine_quant_fp8_static_bf16,
                                    (x.data_ptr(), act.data_ptr(), d["eps"], rows, dim,
@@ -211,21 +275,28 @@ class Producer:
         if st != 0:
             raise RuntimeError(f"{self.name}: status {st}")
 
+    def launch_floor(self, i, stream):
+        fn, args = self.floor_calls[i % self.sets]
+        st = fn(*args, stream)
+        if st != 0:
+            raise RuntimeError(f"{self.name} floor: status {st}")
+
 
 def sets_for(nbytes, cold):
     return max(2, math.ceil(COLD_FOOTPRINT / nbytes)) if cold else 1
 
 
-def time_producer(prod, steps, warmup, use_graph, torch, stream):
+def time_producer(prod, steps, warmup, use_graph, torch, stream, floor=False):
     """Average us per step over exactly `steps` launches on `stream` (a
     dedicated stream, as a pipeline would use), measured with HIP events
     recorded on that stream.  With a graph, the `steps` launches are captured
     once and the graph is replayed once untimed (upload) before the timed
-    replay."""
+    replay.  floor=True times the memory-only counterparts instead."""
     h = stream.cuda_stream
+    launch = prod.launch_floor if floor else prod.launch
     with torch.cuda.stream(stream):
         for i in range(warmup):
-            prod.launch(i, h)
+            launch(i, h)
         torch.cuda.synchronize()
         g = None
         if use_graph:
@@ -233,7 +304,7 @@ def time_producer(prod, steps, warmup, use_graph, torch, stream):
             with torch.cuda.graph(g, stream=torch.cuda.Stream()):
                 hh = torch.cuda.current_stream().cuda_stream
                 for i in range(steps):
-                    prod.launch(i, hh)
+                    launch(i, hh)
             g.replay()
             torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -243,7 +314,7 @@ def time_producer(prod, steps, warmup, use_graph, torch, stream):
             g.replay()
         else:
             for i in range(steps):
-                prod.launch(i, h)
+                launch(i, h)
         t1.record(stream)
         torch.cuda.synchronize()
     del g
@@ -420,6 +491,9 @@ def main():
     results = {}
     head_inputs = None
     stream = torch.cuda.Stream()
+    F = None if a.no_floor else floor_lib()
+    if F is None and not a.no_floor:
+        print("# libalnp_floor.so not built: no practical floors", file=sys.stderr, flush=True)
     for name in names:
         if name == "ln_fp8_2520x3072":
             d = inputs.make("ln", rows=2520, dim=3072)
@@ -437,14 +511,25 @@ def main():
         r = {"bytes": nbytes}
         for mode in modes:
             sets = sets_for(nbytes, mode == "cold")
-            prod = Producer(name, d, sets, torch, alnp)
+            prod = Producer(name, d, sets, torch, alnp, F if mode == "cold" else None)
             us = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream)
             r[mode] = {"us_per_call": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
                        "sets": sets, "footprint_mb": round(sets * nbytes / 2**20, 1)}
+            if prod.floor_calls:
+                fus = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, floor=True)
+                r[mode]["floor_us"] = round(fus, 3)
+                r[mode]["floor_frac_of_peak"] = round(nbytes / fus / 1e3 / HBM_PEAK_GBS, 4)
+                r[mode]["frac_of_floor"] = round(fus / us, 4)
             del prod
             torch.cuda.empty_cache()
+        floor_note = ""
+        if "cold" in r and "floor_us" in r["cold"]:
+            c = r["cold"]
+            floor_note = (f"; memory-only floor {c['floor_us']} us "
+                          f"({100 * c['floor_frac_of_peak']:.1f}% of peak), "
+                          f"kernel at {100 * c['frac_of_floor']:.1f}% of it")
         print(f"# {name}: " + ", ".join(f"{m} {r[m]['us_per_call']} us ({r[m]['gbs']} GB/s)"
-                                        for m in modes), file=sys.stderr, flush=True)
+                                        for m in modes) + floor_note, file=sys.stderr, flush=True)
         results[name] = r
 
     if head not in results or "cold" not in results[head] or "warm" not in results[head]:
@@ -482,6 +567,13 @@ def main():
                      "algorithmic_bytes_per_launch": h["bytes"]},
         "rows": {k: v for k, v in results.items() if k != head},
     }
+    if "floor_us" in h["cold"]:
+        c = h["cold"]
+        line["roofline"]["practical_floor"] = {
+            "us": c["floor_us"], "achieved": round(h["bytes"] / c["floor_us"] / 1e3, 1),
+            "frac_of_peak": c["floor_frac_of_peak"], "kernel_frac_of_floor": c["frac_of_floor"],
+            "what": "memory-only counterpart (libalnp_floor.so): the same loads, stores and "
+                    "launch shape with no arithmetic, timed the same way"}
     if not a.no_overhead and not a.only_headline and not a.only:
         line["launch_overhead"] = launch_overhead(torch, alnp, inputs, stream)
     if not a.no_cpu_baseline:

@@ -1,4 +1,6 @@
-"""Build libalnp.so (the HIP producers and their C ABI) for gfx950 in-tree.
+"""Build libalnp.so (the HIP producers and their C ABI) for gfx950 in-tree,
+and libalnp_floor.so (memory-only counterparts of the producers, which the
+benchmark times beside them; linked against libalnp.so for its row shapes).
 
     python -m dit_adaptive_layernorm_amd.build      # or build() from Python
 
@@ -19,7 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libalnp.so")
+FLOOR_LIB = os.path.join(PKG, "libalnp_floor.so")
 SOURCES = ["producers.hip", "fp4.hip", "rmsmod.hip", "modulation6.hip", "residual.hip", "abi.hip"]
+FLOOR_SOURCE = "floor.hip"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -44,12 +48,13 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+def build(verbose: bool = False, jobs: int = 7) -> str:
     with tempfile.TemporaryDirectory(prefix="alnp_build_") as tmp:
         objs, procs = [], []
-        for src in SOURCES:
+        for src in SOURCES + [FLOOR_SOURCE]:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            objs.append(obj)
+            if src != FLOOR_SOURCE:
+                objs.append(obj)
             procs.append((src, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
         # Compile the translation units in parallel.
         from concurrent.futures import ThreadPoolExecutor
@@ -58,6 +63,11 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
         tmp_lib = LIB + ".tmp"
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB)
+        tmp_floor = FLOOR_LIB + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+              os.path.join(tmp, FLOOR_SOURCE.replace(".hip", ".o")), f"-L{PKG}", "-lalnp",
+              "-Wl,-rpath,$ORIGIN", "-o", tmp_floor], verbose)
+        os.replace(tmp_floor, FLOOR_LIB)
     return LIB
 
 

@@ -1,0 +1,228 @@
+// floor.hip -- memory-only counterparts of the producers, for measurement.
+//
+// Each kernel here makes the same global loads and stores as a producer, with
+// the same launch geometry (one workgroup per row, the producer's waves and
+// vectors per thread; the six-way token-group mapping), and replaces the
+// method's arithmetic by a few XORs that keep every loaded byte live.  Timed
+// beside a producer on the same buffers, such a kernel gives the time this
+// access pattern takes on the chip with no arithmetic at all: a practical
+// floor for the producer, tighter than bytes / vendor peak, which no kernel
+// reaches once launch cost and latency are counted.  Built into its own
+// library (libalnp_floor.so); nothing here is part of the producers' API.
+#include "rows.hpp"
+
+namespace alnp {
+namespace {
+
+// Output layouts of the row floor.
+enum FloorOut : int {
+    kOutFp8 = 0,    // 1 byte per element
+    kOutNvfp4 = 1,  // dim/2 bytes of codes + dim/16 scale bytes per row
+    kOutBf16 = 2,   // 2 bytes per element
+    kOutMxfp8 = 3,  // 1 byte per element + dim/32 scale bytes per row
+    kOutMxfp4 = 4,  // dim/2 bytes of codes + dim/32 scale bytes per row
+};
+
+struct FloorRowArgs {
+    const uint16_t* x;
+    const uint16_t* a;      // optional second stream (nullptr: none)
+    const uint16_t* b;      // optional third stream
+    int64_t ab_stride;      // elements between rows of a and b (0: one shared vector)
+    int64_t rows;
+    int dim;
+    uint8_t* out;
+    uint8_t* scales;
+};
+
+template <int VPT, int WAVES, int OUT, int NIN>
+__global__ __launch_bounds__(WAVES * 64) void k_floor_rows(FloorRowArgs f)
+{
+    constexpr int T = WAVES * 64;
+    const int t = threadIdx.x;
+    const int64_t row = grid_row();
+    if (row >= f.rows)
+        return;
+    const int dim = f.dim;
+    const int nvec = dim >> 3;
+    const bool stream_ab = f.ab_stride != 0;
+    const uint16_t* xr = f.x + row * dim;
+    const uint16_t* ar = NIN > 1 ? f.a + row * f.ab_stride : nullptr;
+    const uint16_t* br = NIN > 2 ? f.b + row * f.ab_stride : nullptr;
+    uint4 xv[VPT], av[VPT], bv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        xv[v] = ld_row<true>(xr, v * T + t, nvec, v == VPT - 1);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        if (NIN > 1)
+            av[v] = stream_ab ? ld_row<true>(ar, v * T + t, nvec, v == VPT - 1)
+                              : ld_row<false>(ar, v * T + t, nvec, v == VPT - 1);
+        if (NIN > 2)
+            bv[v] = stream_ab ? ld_row<true>(br, v * T + t, nvec, v == VPT - 1)
+                              : ld_row<false>(br, v * T + t, nvec, v == VPT - 1);
+    }
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * T + t;
+        if (v == VPT - 1 && i >= nvec)
+            continue;
+        uint4 w = xv[v];
+        if (NIN > 1) {
+            w.x ^= av[v].x; w.y ^= av[v].y; w.z ^= av[v].z; w.w ^= av[v].w;
+        }
+        if (NIN > 2) {
+            w.x ^= bv[v].x; w.y ^= bv[v].y; w.z ^= bv[v].z; w.w ^= bv[v].w;
+        }
+        if (OUT == kOutBf16) {
+            st_stream(reinterpret_cast<uint16_t*>(f.out) + row * dim + (int64_t)i * 8, w);
+        } else if (OUT == kOutFp8 || OUT == kOutMxfp8) {
+            st_stream(f.out + row * dim + (int64_t)i * 8, make_uint2(w.x ^ w.y, w.z ^ w.w));
+            if (OUT == kOutMxfp8 && (i & 3) == 0)
+                f.scales[row * (dim >> 5) + (i >> 2)] = (uint8_t)w.x;
+        } else {
+            st_stream(f.out + row * (dim >> 1) + (int64_t)i * 4, w.x ^ w.y ^ w.z ^ w.w);
+            if (OUT == kOutNvfp4 && (i & 1) == 0)
+                f.scales[row * (dim >> 4) + (i >> 1)] = (uint8_t)w.x;
+            if (OUT == kOutMxfp4 && (i & 3) == 0)
+                f.scales[row * (dim >> 5) + (i >> 2)] = (uint8_t)w.x;
+        }
+    }
+}
+
+template <int OUT, int NIN>
+hipError_t launch_floor_rows(const FloorRowArgs& f, RowShape rs, hipStream_t s)
+{
+    const dim3 grid = row_grid(f.rows);
+#define ALNP_LAUNCH(V, W) hipLaunchKernelGGL((k_floor_rows<V, W, OUT, NIN>), grid, dim3(W * 64), 0, s, f)
+    ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_floor_nin(const FloorRowArgs& f, int nin, RowShape rs, hipStream_t s)
+{
+    switch (nin) {
+    case 1: return launch_floor_rows<OUT, 1>(f, rs, s);
+    case 2: return launch_floor_rows<OUT, 2>(f, rs, s);
+    default: return launch_floor_rows<OUT, 3>(f, rs, s);
+    }
+}
+
+constexpr int kTokensPerThread = 4;
+
+struct FloorMod6Args {
+    const float* params;  // (tokens, 6, dim)
+    int64_t tokens;
+    int dim;
+    uint16_t* out[6];
+};
+
+// The six-way producer's mapping (thread = one 8-element slot of the six
+// chunks x 4 tokens, every load issued before the first store); the output is
+// the upper half of each fp32 (truncation) instead of the rounded sum.
+__global__ __launch_bounds__(256) void k_floor_mod6(FloorMod6Args a)
+{
+    const int dv = a.dim >> 3;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= 6 * dv)
+        return;
+    const int k = (i >= dv) + (i >= 2 * dv) + (i >= 3 * dv) + (i >= 4 * dv) + (i >= 5 * dv);
+    const int j8 = i - k * dv;
+    uint16_t* out = a.out[0];
+#pragma unroll
+    for (int c = 1; c < 6; ++c)
+        out = k == c ? a.out[c] : out;
+    const int64_t t0 = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * kTokensPerThread;
+    uint4 p0[kTokensPerThread], p1[kTokensPerThread];
+#pragma unroll
+    for (int u = 0; u < kTokensPerThread; ++u) {
+        const int64_t t = t0 + u < a.tokens ? t0 + u : a.tokens - 1;
+        const float* pt = a.params + t * 6 * (int64_t)a.dim + 8 * (int64_t)i;
+        p0[u] = ld_stream(pt);
+        p1[u] = ld_stream(pt + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kTokensPerThread; ++u) {
+        const int64_t t = t0 + u;
+        if (t >= a.tokens)
+            break;
+        uint4 o;
+        o.x = (p0[u].x >> 16) | (p0[u].y & 0xFFFF0000u);
+        o.y = (p0[u].z >> 16) | (p0[u].w & 0xFFFF0000u);
+        o.z = (p1[u].x >> 16) | (p1[u].y & 0xFFFF0000u);
+        o.w = (p1[u].z >> 16) | (p1[u].w & 0xFFFF0000u);
+        st_stream(out + t * a.dim + 8 * (int64_t)j8, o);
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+}  // namespace alnp
+
+using namespace alnp;
+
+// Memory-only row kernel in a row producer's launch shape.
+//   x: (rows, dim) bf16, streamed.  a, b: optional bf16 operand rows (nullptr
+//   for none; b only with a); row r of a starts at a + r * ab_stride elements
+//   (ab_stride 0: one (dim,) vector shared by every row, read through cache).
+//   out_kind: 0 = 1 B/element; 1 = NVFP4 (dim/2 code bytes per row, scales
+//   (rows, dim/16)); 2 = bf16 (rows, dim); 3 = MXFP8 (1 B/element, scales
+//   (rows, dim/32)); 4 = MXFP4 (dim/2 code bytes, scales (rows, dim/32)).
+// Returns 0, or -1 for a shape or pointer the row kernels do not take (dim
+// not a multiple of 32, rows longer than the register-resident row shapes,
+// unaligned pointers), -2 for an unknown out_kind, -6 for a launch failure.
+extern "C" int alnp_floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b,
+                               int64_t ab_stride, int64_t rows, int dim, int out_kind, void* out,
+                               uint8_t* scales, hipStream_t stream)
+{
+    if (rows <= 0)
+        return 0;
+    if (!x || !out || dim <= 0 || dim % 32 != 0 || (b && !a) || ab_stride < 0)
+        return -1;
+    if (!aligned16(x) || !aligned16(out) || (a && !aligned16(a)) || (b && !aligned16(b)))
+        return -1;
+    const bool want_scales = out_kind == kOutNvfp4 || out_kind == kOutMxfp8 || out_kind == kOutMxfp4;
+    if (want_scales && !scales)
+        return -1;
+    const RowShape rs = row_shape(dim);
+    if (rs.vpt == 0)
+        return -1;
+    FloorRowArgs f{x, a, b, ab_stride, rows, dim, static_cast<uint8_t*>(out), scales};
+    const int nin = b ? 3 : a ? 2 : 1;
+    hipError_t e;
+    switch (out_kind) {
+    case kOutFp8: e = launch_floor_nin<kOutFp8>(f, nin, rs, stream); break;
+    case kOutNvfp4: e = launch_floor_nin<kOutNvfp4>(f, nin, rs, stream); break;
+    case kOutBf16: e = launch_floor_nin<kOutBf16>(f, nin, rs, stream); break;
+    case kOutMxfp8: e = launch_floor_nin<kOutMxfp8>(f, nin, rs, stream); break;
+    case kOutMxfp4: e = launch_floor_nin<kOutMxfp4>(f, nin, rs, stream); break;
+    default: return -2;
+    }
+    return e == hipSuccess ? 0 : -6;
+}
+
+// Memory-only six-way kernel: params (tokens, 6, dim) fp32 -> six (tokens,
+// dim) bf16 outputs, the six-way producer's grid.  dim a multiple of 8,
+// 16-byte aligned pointers.  Returns 0, -1 (shape, pointer) or -6.
+extern "C" int alnp_floor_modulation6(const float* params, int64_t tokens, int dim,
+                                      uint16_t* const* out, hipStream_t stream)
+{
+    if (tokens <= 0)
+        return 0;
+    if (!params || !out || dim <= 0 || dim % 8 != 0 || !aligned16(params))
+        return -1;
+    FloorMod6Args a{params, tokens, dim, {}};
+    for (int k = 0; k < 6; ++k) {
+        if (!out[k] || !aligned16(out[k]))
+            return -1;
+        a.out[k] = out[k];
+    }
+    const int64_t slots = 6 * (int64_t)(dim >> 3);
+    const int64_t groups = (tokens + kTokensPerThread - 1) / kTokensPerThread;
+    const int64_t gy = groups < 65535 ? groups : 65535;
+    const dim3 grid((unsigned)((slots + 255) / 256), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
+    hipLaunchKernelGGL(k_floor_mod6, grid, dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}

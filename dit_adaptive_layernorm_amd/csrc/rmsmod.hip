@@ -88,6 +88,103 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_rows(RmsArgs a)
         a.row_rstd[row] = rstd;
 }
 
+// Rows [g * span, g * span + span) of workgroup g, one after another, each
+// as in k_rms_mod_rows (same arithmetic and reduction order, so the same
+// bits).  Consecutive rows mostly share their segment, so the weight and the
+// segment's modulation rows are read once per span into registers and read
+// again only when the segment changes; re-reading them from L2 for every row
+// is what separates the one-row kernel from a plain copy of the activations.
+// The next row's x is requested before the current row is reduced.  The
+// span's table indices come in with one vector load (span <= 64), and the
+// two reduction slots alternate so that one row's partials are not
+// overwritten before every wave has read them.
+template <int VPT, int WAVES, bool W>
+__global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a, int span)
+{
+    __shared__ float red[2][16];
+    constexpr int T = WAVES * 64;
+    constexpr int NW = W ? VPT : 1;
+    const int t = threadIdx.x;
+    const int dim = a.dim;
+    const int nvec = dim >> 3;
+    const int64_t r0 = grid_row() * span;
+    if (r0 >= a.rows)
+        return;  // whole workgroup
+    const int n = (int)min<int64_t>(span, a.rows - r0);
+    const bool tail_ok = (VPT - 1) * T + t < nvec;
+    const int lane = t & (kWave - 1);
+    const int32_t segv = lane < n ? a.seg[r0 + lane] : 0;
+
+    uint4 xv[VPT], wv[NW], scv[VPT], shv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        xv[v] = ld_row<true>(a.x + r0 * dim, v * T + t, nvec, v == VPT - 1);
+    if (W) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            wv[v] = ld_row<false>(a.weight, v * T + t, nvec, v == VPT - 1);
+    }
+    int64_t cur = -1;  // segment whose rows scv / shv hold
+    for (int k = 0; k < n; ++k) {
+        const int64_t row = r0 + k;
+        const int32_t sidx = __builtin_amdgcn_readlane(segv, k);
+        const bool in_range = sidx >= 0 && sidx < a.segments;
+        const int64_t srow = in_range ? sidx : 0;
+        if (srow != cur) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                scv[v] = ld_row<false>(a.scale + srow * dim, v * T + t, nvec, v == VPT - 1);
+                shv[v] = ld_row<false>(a.shift + srow * dim, v * T + t, nvec, v == VPT - 1);
+            }
+            cur = srow;
+        }
+        const bool more = k + 1 < n;
+        uint4 xn[VPT];
+        if (more) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+                xn[v] = ld_row<true>(a.x + (row + 1) * dim, v * T + t, nvec, v == VPT - 1);
+        }
+        float q = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            q = sumsq_bf16x8(xv[v], q);
+        const float rstd = rsqrt_refined(group_sum(q, red[k & 1], WAVES) * a.inv_dim + a.eps);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int i = v * T + t;
+            if (v == VPT - 1 && !tail_ok)
+                continue;
+            float f[8], w8[8], sc[8], sh[8];
+            unpack8(xv[v], f);
+            if (W)
+                unpack8(wv[v], w8);
+            unpack8(scv[v], sc);
+            unpack8(shv[v], sh);
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float n0 = f[2 * e] * rstd, n1 = f[2 * e + 1] * rstd;
+                if (W) {
+                    n0 = n0 * w8[2 * e];
+                    n1 = n1 * w8[2 * e + 1];
+                }
+                o[e] = modulate_bf16x2(pack_bf16x2(n0, n1), sc[2 * e], sc[2 * e + 1], sh[2 * e],
+                                       sh[2 * e + 1]);
+                o[e] = in_range ? o[e] : 0x7FC07FC0u;
+            }
+            st_stream(a.out + row * dim + (int64_t)i * 8, make_uint4(o[0], o[1], o[2], o[3]));
+        }
+        if (t == 0 && a.row_rstd)
+            a.row_rstd[row] = rstd;
+        if (more) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+                xv[v] = xn[v];
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_rms_mod_block(RmsArgs a)
 {
     __shared__ float lds4[4];
@@ -118,9 +215,25 @@ __global__ __launch_bounds__(256) void k_rms_mod_block(RmsArgs a)
 
 // ---- launchers ----------------------------------------------------------------
 
+// Rows per workgroup of k_rms_mod_span, and the row count from which it is
+// used: with fewer rows, one row per workgroup keeps more rows in flight (the
+// span kernel's registers allow about half the waves per SIMD).  Two rows per
+// workgroup was the fastest span on the 37810-row Wan workload (longer spans
+// leave too few rows in flight).
+constexpr int kRmsSpan = 2;
+constexpr int64_t kRmsSpanMinRows = 4096;
+
 template <bool W>
 static hipError_t launch_rms_rows(const RmsArgs& a, RowShape rs, hipStream_t s)
 {
+    if (a.rows >= kRmsSpanMinRows) {
+        const dim3 grid = row_grid((a.rows + kRmsSpan - 1) / kRmsSpan);
+#define ALNP_LAUNCH(V, WV) \
+    hipLaunchKernelGGL((k_rms_mod_span<V, WV, W>), grid, dim3(WV * 64), 0, s, a, kRmsSpan)
+        ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+        return hipGetLastError();
+    }
     const dim3 grid = row_grid(a.rows);
 #define ALNP_LAUNCH(V, WV) hipLaunchKernelGGL((k_rms_mod_rows<V, WV, W>), grid, dim3(WV * 64), 0, s, a)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)

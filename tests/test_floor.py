@@ -1,0 +1,144 @@
+"""The memory-only counterparts of the producers (libalnp_floor.so), which the
+benchmark times beside them as a practical floor.  CPU: the library loads,
+exports its two launchers and rejects what the row kernels do not take
+before touching the GPU.  GPU: every floor kernel stores exactly the bytes its
+producer stores (all output and scale bytes, nothing else), checked against a
+numpy model of its XOR pattern."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PATH = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "libalnp_floor.so")
+FP8, NVFP4, BF16, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+
+
+def floor_lib():
+    if not os.path.exists(PATH):
+        pytest.fail("libalnp_floor.so is not built (run the build)")
+    F = ctypes.CDLL(PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    F.alnp_floor_rows.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    F.alnp_floor_rows.restype = ctypes.c_int
+    F.alnp_floor_modulation6.argtypes = [vp, i64, ctypes.c_int, ctypes.POINTER(vp), vp]
+    F.alnp_floor_modulation6.restype = ctypes.c_int
+    return F
+
+
+def test_floor_library_exports_and_rejects_bad_arguments():
+    F = floor_lib()
+    A, B = 1 << 12, 1 << 13  # aligned stand-in addresses: never dereferenced here
+    assert F.alnp_floor_rows(A, None, None, 0, 0, 64, FP8, B, None, None) == 0   # no rows: no-op
+    assert F.alnp_floor_rows(None, None, None, 0, 4, 64, FP8, B, None, None) == -1
+    assert F.alnp_floor_rows(A, None, None, 0, 4, 48, FP8, B, None, None) == -1  # dim % 32
+    assert F.alnp_floor_rows(A + 4, None, None, 0, 4, 64, FP8, B, None, None) == -1
+    assert F.alnp_floor_rows(A, None, A, 0, 4, 64, FP8, B, None, None) == -1     # b without a
+    assert F.alnp_floor_rows(A, None, None, -1, 4, 64, FP8, B, None, None) == -1
+    for kind in (NVFP4, MXFP8, MXFP4):
+        assert F.alnp_floor_rows(A, None, None, 0, 4, 64, kind, B, None, None) == -1
+    assert F.alnp_floor_rows(A, None, None, 0, 4, 64, 9, B, None, None) == -2
+    assert F.alnp_floor_rows(A, None, None, 0, 4, 1 << 21, FP8, B, None, None) == -1
+    outs = (ctypes.c_void_p * 6)(*([B] * 6))
+    assert F.alnp_floor_modulation6(A, 0, 64, outs, None) == 0
+    assert F.alnp_floor_modulation6(A, 4, 60, outs, None) == -1
+    outs[3] = None
+    assert F.alnp_floor_modulation6(A, 4, 64, outs, None) == -1
+
+
+def xor_words(x, a=None, b=None):
+    """(rows, dim) uint16 streams -> (rows, dim/8, 4) uint32 words x ^ a ^ b."""
+    w = np.ascontiguousarray(x).view(np.uint32).reshape(x.shape[0], -1, 4).copy()
+    for s in (a, b):
+        if s is not None:
+            w ^= np.broadcast_to(np.ascontiguousarray(s), x.shape).copy().view(np.uint32).reshape(w.shape)
+    return w
+
+
+def expected_rows(kind, x, a=None, b=None):
+    rows, dim = x.shape
+    w = xor_words(x, a, b)
+    if kind == BF16:
+        return w.reshape(rows, -1).view(np.uint16).reshape(rows, dim), None
+    if kind in (FP8, MXFP8):
+        out = np.stack([w[..., 0] ^ w[..., 1], w[..., 2] ^ w[..., 3]], -1).reshape(rows, -1)
+        out = out.view(np.uint8).reshape(rows, dim)
+    else:
+        out = (w[..., 0] ^ w[..., 1] ^ w[..., 2] ^ w[..., 3]).view(np.uint8).reshape(rows, dim // 2)
+    lo = (w[..., 0] & 0xFF).astype(np.uint8)
+    if kind == NVFP4:
+        return out, lo[:, 0::2]
+    if kind in (MXFP8, MXFP4):
+        return out, lo[:, 0::4]
+    return out, None
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind,nin,stride_kind,rows,dim", [
+    (FP8, 3, "ptok", 5, 3072), (FP8, 3, "bcast", 3, 2048), (FP8, 1, "none", 4, 3072),
+    (FP8, 3, "table", 3, 3072), (NVFP4, 1, "none", 4, 3072), (BF16, 1, "none", 3, 5376),
+    (MXFP8, 3, "ptok", 3, 3072), (MXFP8, 3, "table", 2, 3072), (MXFP4, 1, "none", 3, 3072),
+    (FP8, 3, "ptok", 3, 96), (NVFP4, 1, "none", 2, 96), (BF16, 1, "none", 2, 160),
+])
+def test_floor_rows_store_the_producers_bytes(kind, nin, stride_kind, rows, dim):
+    import torch
+    F = floor_lib()
+    print(f"floor rows kind={kind} nin={nin} {stride_kind} {rows}x{dim}", flush=True)
+    r = np.random.default_rng(kind * 100 + rows + dim)
+    u16 = lambda shape: r.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    dev = lambda h: torch.from_numpy(h.view(np.int16)).cuda()
+    x = u16((rows, dim))
+    chunks, si, hi = 6, 1, 4
+    if stride_kind == "table":
+        temb = u16((rows, chunks, dim))
+        a_h, b_h = temb[:, si, :], temb[:, hi, :]
+        t_d = dev(temb)
+        a_ptr = t_d.data_ptr() + 2 * si * dim
+        b_ptr = t_d.data_ptr() + 2 * hi * dim
+        stride = chunks * dim
+    elif stride_kind in ("ptok", "bcast"):
+        shape = (rows, dim) if stride_kind == "ptok" else (dim,)
+        a_h, b_h = u16(shape), u16(shape)
+        a_d, b_d = dev(a_h), dev(b_h)
+        a_ptr, b_ptr = a_d.data_ptr(), b_d.data_ptr()
+        stride = dim if stride_kind == "ptok" else 0
+    else:
+        a_h = b_h = None
+        a_ptr = b_ptr = None
+        stride = 0
+    want, want_s = expected_rows(kind, x, a_h, b_h)
+    out = torch.full((want.size * want.itemsize,), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = None
+    if want_s is not None:
+        scales = torch.full((want_s.size,), 0x5A, dtype=torch.uint8, device="cuda")
+    x_d = dev(x)
+    st = F.alnp_floor_rows(x_d.data_ptr(), a_ptr, b_ptr, stride, rows, dim, kind, out.data_ptr(),
+                           scales.data_ptr() if scales is not None else None,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, np.ascontiguousarray(want).view(np.uint8).reshape(-1))
+    if want_s is not None:
+        assert np.array_equal(scales.cpu().numpy(), want_s.reshape(-1))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tokens,dim", [(9, 256), (12, 3072)])
+def test_floor_modulation6_stores_the_six_outputs(tokens, dim):
+    import torch
+    F = floor_lib()
+    print(f"floor modulation6 {tokens}x{dim}", flush=True)
+    r = np.random.default_rng(tokens + dim)
+    p = r.integers(0, 1 << 32, size=(tokens, 6, dim), dtype=np.uint32)
+    p_d = torch.from_numpy(p.view(np.int32)).cuda()
+    outs = [torch.full((tokens, dim), 0x1234, dtype=torch.int16, device="cuda") for _ in range(6)]
+    arr = (ctypes.c_void_p * 6)(*[o.data_ptr() for o in outs])
+    st = F.alnp_floor_modulation6(p_d.data_ptr(), tokens, dim, arr,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for k in range(6):
+        want = (p[:, k, :] >> 16).astype(np.uint16)
+        assert np.array_equal(outs[k].cpu().numpy().view(np.uint16), want), k

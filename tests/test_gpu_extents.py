@@ -1,7 +1,9 @@
 """Extents of the launch mapping, against the oracle through the C ABI: row
 counts past the 65535 workgroups one grid dimension holds (the row kernels
-then use a second grid dimension), and rows of 2^20 elements, which go to the
-workgroup-per-row fallback.  Rows on both sides of each boundary are checked."""
+then use a second grid dimension; the table form and the RMSNorm producer's
+span kernel hold two rows per workgroup), and rows of 2^20 elements, which go
+to the workgroup-per-row fallback.  Rows on both sides of each boundary are
+checked."""
 import numpy as np
 import pytest
 import torch
@@ -64,13 +66,17 @@ def test_fp4_rows_past_one_grid_dimension(orc):
     assert_codes_close(host_u8(sf)[sel], rs, e4m3_ordinal, "fp4 scales")
 
 
-def test_rmsmod_rows_past_one_grid_dimension(orc):
-    rows, dim = 70001, 64
+@pytest.mark.parametrize("rows", [70001, 140003])
+def test_rmsmod_rows_past_one_grid_dimension(orc, rows):
+    # Two rows per workgroup from 4096 rows: 140003 rows need a second grid
+    # dimension, 70001 rows do not.
+    dim = 64
+    print(f"rmsmod rows={rows} dim={dim}", flush=True)
     d = inputs.make("rmsmod", rows=rows, dim=dim, seed=7)
     o = alnp.rms_norm_modulate_seg_bf16(dev_bf16(d["x"]), dev_bf16(d["weight"]),
                                         dev_bf16(d["scale"]), dev_bf16(d["shift"]),
                                         torch.from_numpy(d["seg"]).cuda())
-    sel = boundary_rows(rows)
+    sel = boundary_rows(rows, per_group=2)
     ref = orc.rms_modulate_seg(d["x"][sel], d["weight"], d["scale"], d["shift"], d["seg"][sel])[0]
     got = host_u16(o)[sel]
     assert np.mean(got == ref) >= 0.999

@@ -3,7 +3,9 @@ shift rows, bf16 operations) with the oracle through the C ABI: small and
 ragged shapes with and without the RMSNorm weight (row kernel and fallback),
 the 37810 x 5376 three-segment workload on sampled rows including the segment
 boundaries, out-of-range segment indices, unaligned operands, and batch
-invariance.
+invariance.  From 4096 rows the producer runs rows in spans of two per
+workgroup (operands kept across the span): that path is checked with segment
+indices that change inside spans, and against the one-row kernel bit for bit.
 
 The kernel's fp32 row statistic can differ from the oracle's double one in its
 last bit, which moves a bf16 RMSNorm output n to an adjacent value in rare
@@ -132,3 +134,30 @@ def test_batch_invariance():
     for r0, bs in ((0, 1), (99, 2), (100, 7), (513, 64), (600, 100)):
         sub = {k: (v[r0:r0 + bs] if k in ("x", "seg") else v) for k, v in d.items()}
         assert np.array_equal(run_gpu(sub)[0], full[r0:r0 + bs])
+
+
+@pytest.mark.parametrize("weight", [True, False])
+@pytest.mark.parametrize("dim", [1536, 200])
+def test_span_path_with_changing_segments(orc, weight, dim):
+    # 4097 rows: the span kernel, with a last span of one row; segment indices
+    # drawn per row (they change inside spans), some of them out of range.
+    rows = 4097
+    print(f"rmsmod span rows={rows} dim={dim} weight={weight}", flush=True)
+    d = inputs.make("rmsmod", rows=rows, dim=dim, seed=13 + dim, segments=4)
+    seg = d["seg"].copy()
+    seg[[5, 6, 1000, 4095, 4096]] = [-1, 4, 1 << 30, -7, 9]
+    got = run_gpu(d, weight=weight, seg=seg)
+    assert np.all(got[0][[5, 6, 1000, 4095, 4096]] == 0x7FC0)
+    check(orc, got, d, weight=weight, seg=seg, what=f"span path {rows}x{dim}")
+
+
+def test_span_and_row_kernels_agree():
+    # The same rows through the span kernel (4100 rows) and the one-row kernel
+    # (calls of fewer than 4096 rows): identical outputs and row statistics.
+    d = inputs.make("rmsmod", rows=4100, dim=5376, seed=14, layout="h3")
+    full, full_rstd = run_gpu(d)
+    for r0, bs in ((0, 2001), (2001, 2099)):
+        sub = {k: (v[r0:r0 + bs] if k in ("x", "seg") else v) for k, v in d.items()}
+        out, rstd = run_gpu(sub)
+        assert np.array_equal(out, full[r0:r0 + bs])
+        assert np.array_equal(rstd.view(np.uint32), full_rstd[r0:r0 + bs].view(np.uint32))
