@@ -197,6 +197,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 // before the row loads so that the LDS fill does not wait behind them.
 constexpr int kTableRows = 2;     // rows per workgroup
 constexpr int kTableMaxDim = 8192; // 2 table rows * 8192 * 4 B = 64 KiB of LDS
+// Up to this many rows the table form runs the rows kernel instead, which
+// holds each thread's table values in registers: with few rows resident,
+// registers are not what limits the kernel, and skipping the LDS staging and
+// its barrier shortens the call (51 x 1536: 3.28 -> 2.31 us; 256 x 3072:
+// 3.48 -> 2.72 us; even at 512 rows, slower from 1024).  Both kernels sum the
+// row statistics in the same order, so the switch changes no bits.
+constexpr int64_t kTableLdsMinRows = 513;
 
 template <int VPT, int WAVES, int R = kTableRows, bool MX = false>
 __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
@@ -463,7 +470,8 @@ hipError_t launch_adaln_fp8(const Fp8Args& args, int form, bool fast, hipStream_
     Fp8Args a = args;
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
-    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256)
+    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256 &&
+        a.rows >= kTableLdsMinRows)
         return launch_fp8_table_lds(a, rs, s);
     if (rs.vpt > 0) {
         switch (form) {
@@ -505,7 +513,8 @@ hipError_t launch_mxfp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
     Fp8Args a = args;
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
-    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256) {
+    if (rs.vpt > 0 && form == kTable && a.dim <= kTableMaxDim && rs.threads <= 256 &&
+        a.rows >= kTableLdsMinRows) {
         const dim3 grid = row_grid((a.rows + kTableRows - 1) / kTableRows);
         const size_t lds = 2 * (size_t)a.dim * sizeof(float);
 #define ALNP_LAUNCH(V, W) launch_table_lds_mx_shape<V, W>(a, grid, lds, s)

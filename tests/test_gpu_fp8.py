@@ -115,8 +115,10 @@ def test_broadcast_equals_replicated_per_token_bitwise():
     assert np.array_equal(o1, o2)
 
 
-def test_table_zero_equals_per_token_chunks_bitwise():
-    d = inputs.make("table", rows=70, dim=3072, seed=7, shift_idx=5, scale_idx=3)
+@pytest.mark.parametrize("rows", [70, 600])
+def test_table_zero_equals_per_token_chunks_bitwise(rows):
+    # 70 rows: the table form on the rows kernel; 600 rows: on the LDS kernel.
+    d = inputs.make("table", rows=rows, dim=3072, seed=7, shift_idx=5, scale_idx=3)
     x, temb, a = dev_bf16(d["x"]), dev_bf16(d["temb"]), act()
     zero = torch.zeros(6, 3072, dtype=torch.float32, device="cuda")
     o1 = host_u8(alnp.ada_layer_norm_quant_fp8_ptok_table_bf16(x, temb, zero, a, 5, 3))
@@ -139,6 +141,19 @@ def test_batch_invariance_and_determinism():
             part = host_u8(alnp.ada_layer_norm_quant_fp8_ptok_bf16(
                 x[r0:r1], s[r0:r1], h[r0:r1], a))
             assert np.array_equal(part, full[r0:r1]), (bs, r0)
+
+
+def test_table_batch_invariance_across_kernels():
+    """The table form runs the rows kernel up to 512 rows and the LDS-staged
+    kernel above: one 1030-row call and calls of at most 512 rows give the
+    same bytes and row statistics."""
+    d = inputs.make("table", rows=1030, dim=3072, seed=9, shift_idx=2, scale_idx=4)
+    full = run_gpu("table", d, 1030, 3072)
+    for r0, bs in ((0, 512), (512, 511), (1023, 7), (300, 1)):
+        sub = {k: (v[r0:r0 + bs] if k in ("x", "temb") else v) for k, v in d.items()}
+        part = run_gpu("table", sub, bs, 3072)
+        for p, f in zip(part, full):
+            assert np.array_equal(p, f[r0:r0 + bs]), (r0, bs)
 
 
 def test_empty_rows_is_noop():

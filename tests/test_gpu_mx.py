@@ -184,6 +184,16 @@ def test_batch_invariance_and_determinism():
         assert np.array_equal(c4, full4[0][r0:r0 + bs]) and np.array_equal(s4, full4[1][r0:r0 + bs])
 
 
+def test_mxfp8_table_batch_invariance_across_kernels():
+    # Rows kernel up to 512 rows, LDS-staged table kernel above: same bytes.
+    d = inputs.make("table", rows=1030, dim=3072, seed=47, shift_idx=3, scale_idx=0)
+    full_o, full_s = run_mxfp8("table", d)
+    for r0, bs in ((0, 512), (512, 511), (1023, 7)):
+        sub = {k: (v[r0:r0 + bs] if k in ("x", "temb") else v) for k, v in d.items()}
+        o, sc = run_mxfp8("table", sub)
+        assert np.array_equal(o, full_o[r0:r0 + bs]) and np.array_equal(sc, full_s[r0:r0 + bs]), (r0, bs)
+
+
 def test_infinite_block_maximum(orc):
     # A huge broadcast scale overflows y (and its bf16 stage) to +-inf in some
     # blocks: the block maximum is infinite, E = 127, infinities saturate and
