@@ -12,6 +12,13 @@ This module only checks tensors and marshals pointers: every step runs in
 the HIP kernels, on the current torch stream.  If libalnp.so is missing or
 cannot be loaded the functions raise; there is no CPU fallback.
 
+Two bindings do that marshalling.  The compiled one (_torch_binding, from
+csrc/torch_binding.cpp) makes the checks and the C-ABI call in C++; when it
+is built, the public functions are its functions.  The ctypes functions
+defined below make the same checks in Python and stay available as
+`ctypes_api`; they are the public functions only where the compiled binding
+has not been built.  `binding()` says which one is in use.
+
 FP4 block scales come in two layouts: the README's *_swizzled_* functions
 write the 128x4 tiled layout (buffer size swizzled_sf_size(rows, dim)); the
 functions without "swizzled" write plain row-major (rows, dim // 16) scales
@@ -21,6 +28,8 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sysconfig
+import types
 
 import torch
 
@@ -569,6 +578,42 @@ def quant_fp8_static_f32(v, act_scale, out=None):
     return out
 
 
+# ---- compiled binding ------------------------------------------------------------
+
+_COMPILED_NAMES = (
+    "ada_layer_norm_quant_fp8_bf16", "ada_layer_norm_quant_fp8_ptok_bf16",
+    "ada_layer_norm_quant_fp8_ptok_table_bf16", "ada_layer_norm_quant_fp8_modfp8_bf16",
+    "awq_ada_layer_norm_quant_fp8_bf16", "layer_norm_no_affine_quant_fp8_static_bf16",
+    "quant_fp8_static_f32", "layer_norm_no_affine_quant_nvfp4_bf16",
+    "layer_norm_no_affine_quant_nvfp4_swizzled_bf16", "ada_layer_norm_quant_nvfp4_bf16",
+    "ada_layer_norm_quant_nvfp4_swizzled_bf16", "ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16",
+    "layer_norm_no_affine_quant_mxfp8_bf16", "ada_layer_norm_quant_mxfp8_bf16",
+    "ada_layer_norm_quant_mxfp8_ptok_bf16", "ada_layer_norm_quant_mxfp8_ptok_table_bf16",
+    "layer_norm_no_affine_quant_mxfp4_bf16", "ada_layer_norm_quant_mxfp4_bf16",
+    "adaln_modulation6_bf16", "gated_residual_bf16", "rms_norm_modulate_seg_bf16",
+)
+
+# The ctypes functions, whichever binding is public.
+ctypes_api = types.SimpleNamespace(**{_n: globals()[_n] for _n in _COMPILED_NAMES})
+
+_compiled = None
+_BINDING_PATH = os.path.join(_PKG, "_torch_binding" + sysconfig.get_config_var("EXT_SUFFIX"))
+if os.path.exists(_BINDING_PATH):
+    # Built, so it must load: a binding that fails to import is an error, not
+    # a reason to fall back silently.
+    from . import _torch_binding as _compiled
+
+    _compiled.set_error_class(AlnpError)
+    for _n in _COMPILED_NAMES:
+        globals()[_n] = getattr(_compiled, _n)
+
+
+def binding() -> str:
+    """"compiled" when the public functions are the compiled binding's,
+    "ctypes" otherwise."""
+    return "compiled" if _compiled is not None else "ctypes"
+
+
 __all__ = [
     "ada_layer_norm_quant_fp8_bf16", "ada_layer_norm_quant_fp8_ptok_bf16",
     "ada_layer_norm_quant_fp8_ptok_table_bf16", "ada_layer_norm_quant_fp8_modfp8_bf16",
@@ -582,5 +627,5 @@ __all__ = [
     "ada_layer_norm_quant_mxfp8_ptok_bf16", "ada_layer_norm_quant_mxfp8_ptok_table_bf16",
     "layer_norm_no_affine_quant_mxfp4_bf16",
     "ada_layer_norm_quant_mxfp4_bf16", "mx_scale_size",
-    "lib", "AlnpError", "SIGNATURES",
+    "lib", "AlnpError", "SIGNATURES", "binding", "ctypes_api",
 ]

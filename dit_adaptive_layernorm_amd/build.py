@@ -1,6 +1,8 @@
 """Build libalnp.so (the HIP producers and their C ABI) for gfx950 in-tree,
-and libalnp_floor.so (memory-only counterparts of the producers, which the
-benchmark times beside them; linked against libalnp.so for its row shapes).
+libalnp_floor.so (memory-only counterparts of the producers, which the
+benchmark times beside them; linked against libalnp.so for its row shapes),
+and the compiled binding _torch_binding (the package's functions in C++ over
+the C ABI: host code only, built with the C++ compiler against torch).
 
     python -m dit_adaptive_layernorm_amd.build      # or build() from Python
 
@@ -24,6 +26,8 @@ LIB = os.path.join(PKG, "libalnp.so")
 FLOOR_LIB = os.path.join(PKG, "libalnp_floor.so")
 SOURCES = ["producers.hip", "fp4.hip", "rmsmod.hip", "modulation6.hip", "residual.hip", "abi.hip"]
 FLOOR_SOURCE = "floor.hip"
+BINDING_SOURCE = "torch_binding.cpp"
+CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -48,6 +52,36 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
+def _binding_commands(obj: str, tmp_so: str):
+    """Compile and link commands of the compiled binding."""
+    import sysconfig
+
+    import torch
+
+    tdir = os.path.dirname(torch.__file__)
+    cflags = [
+        "-O2", "-std=c++17", "-fPIC", "-Wall",
+        "-DTORCH_EXTENSION_NAME=_torch_binding", "-DTORCH_API_INCLUDE_EXTENSION_H",
+        f"-D_GLIBCXX_USE_CXX11_ABI={int(torch._C._GLIBCXX_USE_CXX11_ABI)}",
+        # torch's ROCm headers (c10/hip/HIPStream.h) and the HIP runtime
+        # headers under them expect the macros of a ROCm build of torch when
+        # the compiler is not hipcc.
+        "-DUSE_ROCM=1", "-D__HIP_PLATFORM_AMD__=1",
+        f"-I{tdir}/include", f"-I{tdir}/include/torch/csrc/api/include",
+        f"-I{sysconfig.get_paths()['include']}", "-I/opt/rocm/include", f"-I{INCLUDE}",
+    ]
+    compile_cmd = [CXX, *cflags, "-c", os.path.join(CSRC, BINDING_SOURCE), "-o", obj]
+    link_cmd = [CXX, "-shared", obj, "-o", tmp_so, f"-L{tdir}/lib", "-lc10", "-lc10_hip",
+                "-ltorch", "-ltorch_cpu", "-ltorch_hip", "-ltorch_python", f"-L{PKG}", "-lalnp",
+                "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{tdir}/lib"]
+    return compile_cmd, link_cmd
+
+
+def binding_path() -> str:
+    import sysconfig
+    return os.path.join(PKG, "_torch_binding" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
 def build(verbose: bool = False, jobs: int = 7) -> str:
     with tempfile.TemporaryDirectory(prefix="alnp_build_") as tmp:
         objs, procs = [], []
@@ -56,6 +90,10 @@ def build(verbose: bool = False, jobs: int = 7) -> str:
             if src != FLOOR_SOURCE:
                 objs.append(obj)
             procs.append((src, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        binding_so = binding_path()
+        bind_compile, bind_link = _binding_commands(os.path.join(tmp, "torch_binding.o"),
+                                                    binding_so + ".tmp")
+        procs.append((BINDING_SOURCE, bind_compile))
         # Compile the translation units in parallel.
         from concurrent.futures import ThreadPoolExecutor
         with ThreadPoolExecutor(max(1, jobs)) as ex:
@@ -68,6 +106,8 @@ def build(verbose: bool = False, jobs: int = 7) -> str:
               os.path.join(tmp, FLOOR_SOURCE.replace(".hip", ".o")), f"-L{PKG}", "-lalnp",
               "-Wl,-rpath,$ORIGIN", "-o", tmp_floor], verbose)
         os.replace(tmp_floor, FLOOR_LIB)
+        _run(bind_link, verbose)
+        os.replace(binding_so + ".tmp", binding_so)
     return LIB
 
 
