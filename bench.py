@@ -580,8 +580,8 @@ def main():
         line["roofline"]["practical_floor"] = {
             "us": c["floor_us"], "achieved": round(h["bytes"] / c["floor_us"] / 1e3, 1),
             "frac_of_peak": c["floor_frac_of_peak"], "kernel_frac_of_floor": c["frac_of_floor"],
-            "what": "memory-only counterpart (libalnp_floor.so): the same loads, stores and "
-                    "launch shape with no arithmetic, timed the same way"}
+            "what": "memory-only counterpart (libalnp_floor.so): the same loads and stores in "
+                    "the producer's row shape, no arithmetic, timed the same way"}
     if not a.no_overhead and not a.only_headline and not a.only:
         line["launch_overhead"] = launch_overhead(torch, alnp, inputs, stream)
     if not a.no_cpu_baseline:

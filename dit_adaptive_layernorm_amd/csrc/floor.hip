@@ -1,9 +1,11 @@
 // floor.hip -- memory-only counterparts of the producers, for measurement.
 //
-// Each kernel here makes the same global loads and stores as a producer, with
-// the same launch geometry (one workgroup per row, the producer's waves and
-// vectors per thread; the six-way token-group mapping), and replaces the
-// method's arithmetic by a few XORs that keep every loaded byte live.  Timed
+// Each kernel here makes the same global loads and stores as a producer, in
+// the producer's row shape (its waves per row and vectors per thread, one
+// workgroup per row; the six-way token-group mapping), and replaces the
+// method's arithmetic by a few XORs that keep every loaded byte live.  The
+// table and RMSNorm producers put two rows in a workgroup on large calls;
+// their floors keep one row per workgroup, the plain streaming layout.  Timed
 // beside a producer on the same buffers, such a kernel gives the time this
 // access pattern takes on the chip with no arithmetic at all: a practical
 // floor for the producer, tighter than bytes / vendor peak, which no kernel
