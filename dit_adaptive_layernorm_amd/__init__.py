@@ -74,6 +74,12 @@ SIGNATURES = {
     "alnp_mx_scale_size": ([_I64, _I64], _I64),
     "alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16": (
         [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16": (
+        [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_awq_ada_layer_norm_quant_mxfp8_bf16": (
+        [_P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16": (
+        [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "alnp_gated_residual_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "alnp_rms_norm_modulate_seg_bf16": (
         [_P, _P, _P, _P, _P, _I64, _F, _I64, _I64, _P, _P, _P], _I),
@@ -467,6 +473,40 @@ def ada_layer_norm_quant_mxfp8_ptok_table_bf16(x, temb, table, shift_idx, scale_
     return out, scales
 
 
+def ada_layer_norm_quant_mxfp8_modfp8_bf16(x, scale_fp8, shift_fp8, scale_deq, shift_deq,
+                                           eps=1e-5, out=None, scales=None, row_mean=None,
+                                           row_rstd=None):
+    """AdaLN with e4m3 (dim,) scale/shift and fp32 device dequantization scalars
+    -> MXFP8."""
+    rows, dim = _x(x)
+    scales = _mx_scales(x, rows, dim, scales)
+    out = _fp8_out(out, x)
+    _check("alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16",
+           lib().alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16(
+               x.data_ptr(), _dev(scale_fp8, "scale_fp8", torch.float8_e4m3fn, (dim,)),
+               _dev(shift_fp8, "shift_fp8", torch.float8_e4m3fn, (dim,)),
+               _scalar(scale_deq, "scale_deq"), _scalar(shift_deq, "shift_deq"), eps, rows, dim,
+               out.data_ptr(), scales.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+               _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return out, scales
+
+
+def awq_ada_layer_norm_quant_mxfp8_bf16(x, scale, shift, inv_s, eps=1e-5, out=None, scales=None,
+                                        row_mean=None, row_rstd=None):
+    """Broadcast AdaLN -> per-channel inv_s (dim,) bf16 -> MXFP8."""
+    rows, dim = _x(x)
+    scales = _mx_scales(x, rows, dim, scales)
+    out = _fp8_out(out, x)
+    _check("alnp_awq_ada_layer_norm_quant_mxfp8_bf16",
+           lib().alnp_awq_ada_layer_norm_quant_mxfp8_bf16(
+               x.data_ptr(), _dev(scale, "scale", torch.bfloat16, (dim,)),
+               _dev(shift, "shift", torch.bfloat16, (dim,)),
+               _dev(inv_s, "inv_s", torch.bfloat16, (dim,)), eps, rows, dim, out.data_ptr(),
+               scales.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+               _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return out, scales
+
+
 def _mxfp4(name, x, scale, shift, eps, packed, scales, row_mean, row_rstd):
     rows, dim = _x(x)
     scales = _mx_scales(x, rows, dim, scales)
@@ -494,6 +534,26 @@ def ada_layer_norm_quant_mxfp4_bf16(x, scale, shift, eps=1e-5, packed=None, scal
     """Broadcast AdaLN -> bf16 stage -> MXFP4; scale, shift (dim,) bf16."""
     return _mxfp4("alnp_ada_layer_norm_quant_mxfp4_bf16", x, scale, shift, eps, packed, scales,
                   row_mean, row_rstd)
+
+
+def ada_layer_norm_quant_mxfp4_modfp8_bf16(x, scale_fp8, shift_fp8, scale_deq, shift_deq,
+                                           eps=1e-5, packed=None, scales=None, row_mean=None,
+                                           row_rstd=None):
+    """AdaLN with e4m3 (dim,) scale/shift and fp32 device dequantization scalars
+    -> bf16 stage -> MXFP4."""
+    rows, dim = _x(x)
+    scales = _mx_scales(x, rows, dim, scales)
+    if packed is None:
+        packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=x.device)
+    _dev(packed, "packed", torch.uint8, (rows, dim // 2))
+    _check("alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16",
+           lib().alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16(
+               x.data_ptr(), _dev(scale_fp8, "scale_fp8", torch.float8_e4m3fn, (dim,)),
+               _dev(shift_fp8, "shift_fp8", torch.float8_e4m3fn, (dim,)),
+               _scalar(scale_deq, "scale_deq"), _scalar(shift_deq, "shift_deq"), eps, rows, dim,
+               packed.data_ptr(), scales.data_ptr(), _opt(row_mean, "row_mean", (rows,)),
+               _opt(row_rstd, "row_rstd", (rows,)), _stream()))
+    return packed, scales
 
 
 # ---- six-way modulation --------------------------------------------------------
@@ -590,6 +650,8 @@ _COMPILED_NAMES = (
     "layer_norm_no_affine_quant_mxfp8_bf16", "ada_layer_norm_quant_mxfp8_bf16",
     "ada_layer_norm_quant_mxfp8_ptok_bf16", "ada_layer_norm_quant_mxfp8_ptok_table_bf16",
     "layer_norm_no_affine_quant_mxfp4_bf16", "ada_layer_norm_quant_mxfp4_bf16",
+    "ada_layer_norm_quant_mxfp8_modfp8_bf16", "awq_ada_layer_norm_quant_mxfp8_bf16",
+    "ada_layer_norm_quant_mxfp4_modfp8_bf16",
     "adaln_modulation6_bf16", "gated_residual_bf16", "rms_norm_modulate_seg_bf16",
 )
 
@@ -601,11 +663,16 @@ _BINDING_PATH = os.path.join(_PKG, "_torch_binding" + sysconfig.get_config_var("
 if os.path.exists(_BINDING_PATH):
     # Built, so it must load: a binding that fails to import is an error, not
     # a reason to fall back silently.
-    from . import _torch_binding as _compiled
+    from . import _torch_binding as _loaded
 
-    _compiled.set_error_class(AlnpError)
-    for _n in _COMPILED_NAMES:
-        globals()[_n] = getattr(_compiled, _n)
+    # A binding built from older sources lacks some functions: it is not used
+    # (the build imports this package before rebuilding it), and binding()
+    # says "ctypes" until it is rebuilt.
+    if all(hasattr(_loaded, _n) for _n in _COMPILED_NAMES):
+        _compiled = _loaded
+        _compiled.set_error_class(AlnpError)
+        for _n in _COMPILED_NAMES:
+            globals()[_n] = getattr(_compiled, _n)
 
 
 def binding() -> str:
@@ -627,5 +694,7 @@ __all__ = [
     "ada_layer_norm_quant_mxfp8_ptok_bf16", "ada_layer_norm_quant_mxfp8_ptok_table_bf16",
     "layer_norm_no_affine_quant_mxfp4_bf16",
     "ada_layer_norm_quant_mxfp4_bf16", "mx_scale_size",
+    "ada_layer_norm_quant_mxfp8_modfp8_bf16", "awq_ada_layer_norm_quant_mxfp8_bf16",
+    "ada_layer_norm_quant_mxfp4_modfp8_bf16",
     "lib", "AlnpError", "SIGNATURES", "binding", "ctypes_api",
 ]

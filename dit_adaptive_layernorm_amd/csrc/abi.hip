@@ -86,17 +86,22 @@ int run_mxfp8(Fp8Args a, int form, void* stream)
     if (int st = check_rows_dim(a.rows, a.dim, 32))
         return st > 0 ? ALNP_OK : st;
     if (!a.x || !a.out || !a.mx_scales ||
-        ((form == alnp::kBcast || form == alnp::kPtok) && (!a.scale || !a.shift)) ||
-        (form == alnp::kTable && (!a.temb || !a.table)))
+        ((form == alnp::kBcast || form == alnp::kPtok || form == alnp::kAwq) &&
+         (!a.scale || !a.shift)) ||
+        (form == alnp::kAwq && !a.inv_s) ||
+        (form == alnp::kTable && (!a.temb || !a.table)) ||
+        (form == alnp::kModFp8 && (!a.scale_fp8 || !a.shift_fp8 || !a.scale_deq || !a.shift_deq)))
         return ALNP_ERR_NULL;
     if (!aligned(a.x, 2) || !aligned(a.scale, 2) || !aligned(a.shift, 2) || !aligned(a.temb, 2) ||
-        !aligned(a.table, 4) || !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
+        !aligned(a.table, 4) || !aligned(a.inv_s, 2) || !aligned(a.scale_deq, 4) ||
+        !aligned(a.shift_deq, 4) || !aligned(a.row_mean, 4) || !aligned(a.row_rstd, 4))
         return ALNP_ERR_ALIGN;
     if (int st = check_eps(a.eps))
         return st;
     const bool fast = a.dim <= alnp::kMaxFastDim && aligned(a.x, 16) && aligned(a.scale, 16) &&
                       aligned(a.shift, 16) && aligned(a.temb, 16) && aligned(a.table, 16) &&
-                      aligned(a.out, 8);
+                      aligned(a.inv_s, 16) && aligned(a.scale_fp8, 8) &&
+                      aligned(a.shift_fp8, 8) && aligned(a.out, 8);
     return launch_status(alnp::launch_mxfp8(a, form, fast, as_stream(stream)));
 }
 
@@ -326,6 +331,22 @@ int alnp_ada_layer_norm_quant_mxfp4_bf16(const uint16_t* x, const uint16_t* scal
     return run_fp4(a, stream);
 }
 
+int alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16(const uint16_t* x, const uint8_t* scale_fp8,
+                                                const uint8_t* shift_fp8, const float* scale_deq,
+                                                const float* shift_deq, float eps, int64_t rows,
+                                                int64_t dim, uint8_t* packed, uint8_t* scales,
+                                                float* row_mean, float* row_rstd, void* stream)
+{
+    Fp4Args a = fp4_args(x, eps, rows, dim, packed, scales, alnp::kSfRowMajor, row_mean, row_rstd);
+    a.mx = 1;
+    a.form = alnp::kModFp8;
+    a.scale_fp8 = scale_fp8;
+    a.shift_fp8 = shift_fp8;
+    a.scale_deq = scale_deq;
+    a.shift_deq = shift_deq;
+    return run_fp4(a, stream);
+}
+
 int alnp_layer_norm_no_affine_quant_mxfp8_bf16(const uint16_t* x, float eps, int64_t rows,
                                                int64_t dim, uint8_t* out, uint8_t* scales,
                                                float* row_mean, float* row_rstd, void* stream)
@@ -357,6 +378,35 @@ int alnp_ada_layer_norm_quant_mxfp8_ptok_bf16(const uint16_t* x, const uint16_t*
     a.scale = scale;
     a.shift = shift;
     return run_mxfp8(a, alnp::kPtok, stream);
+}
+
+int alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16(const uint16_t* x, const uint8_t* scale_fp8,
+                                                const uint8_t* shift_fp8, const float* scale_deq,
+                                                const float* shift_deq, float eps, int64_t rows,
+                                                int64_t dim, uint8_t* out, uint8_t* scales,
+                                                float* row_mean, float* row_rstd, void* stream)
+{
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    a.scale_fp8 = scale_fp8;
+    a.shift_fp8 = shift_fp8;
+    a.scale_deq = scale_deq;
+    a.shift_deq = shift_deq;
+    return run_mxfp8(a, alnp::kModFp8, stream);
+}
+
+int alnp_awq_ada_layer_norm_quant_mxfp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                             const uint16_t* shift, const uint16_t* inv_s,
+                                             float eps, int64_t rows, int64_t dim, uint8_t* out,
+                                             uint8_t* scales, float* row_mean, float* row_rstd,
+                                             void* stream)
+{
+    Fp8Args a = fp8_args(x, nullptr, eps, rows, dim, out, row_mean, row_rstd);
+    a.mx_scales = scales;
+    a.scale = scale;
+    a.shift = shift;
+    a.inv_s = inv_s;
+    return run_mxfp8(a, alnp::kAwq, stream);
 }
 
 int alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16(

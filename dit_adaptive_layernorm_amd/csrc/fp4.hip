@@ -306,11 +306,16 @@ hipError_t launch_fp4(const Fp4Args& args, bool fast, hipStream_t s)
     a.inv_dim = 1.0f / (float)a.dim;
     const RowShape rs = fast ? row_shape(a.dim) : RowShape{0, 0};
     if (a.mx) {
-        if (a.sf_layout != kSfRowMajor || (a.form != kNone && a.form != kBcast))
-            return hipErrorInvalidValue;  // MXFP4: LN or broadcast AdaLN, row-major scales
-        if (rs.vpt > 0)
-            return a.form == kBcast ? launch_fp4_rows<kBcast, false, true>(a, rs, s)
-                                    : launch_fp4_rows<kNone, false, true>(a, rs, s);
+        // MXFP4: LN, broadcast or modfp8 AdaLN, row-major E8M0 scales.
+        if (a.sf_layout != kSfRowMajor || (a.form != kNone && a.form != kBcast && a.form != kModFp8))
+            return hipErrorInvalidValue;
+        if (rs.vpt > 0) {
+            switch (a.form) {
+            case kBcast: return launch_fp4_rows<kBcast, false, true>(a, rs, s);
+            case kModFp8: return launch_fp4_rows<kModFp8, false, true>(a, rs, s);
+            default: return launch_fp4_rows<kNone, false, true>(a, rs, s);
+            }
+        }
         const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
         hipLaunchKernelGGL(k_mxfp4_block, grid, dim3(256), 0, s, a);
         return hipGetLastError();

@@ -377,9 +377,17 @@ __global__ __launch_bounds__(256) void k_mxfp8_block(Fp8Args a, int form)
                      a.table[(int64_t)a.scale_idx * dim + j];
                 sh = ldbf(a.temb, (row * a.chunks + a.shift_idx) * dim + j) +
                      a.table[(int64_t)a.shift_idx * dim + j];
+            } else if (form == kModFp8) {
+                sc = __builtin_amdgcn_cvt_f32_fp8((int)a.scale_fp8[j], 0) * *a.scale_deq;
+                sh = __builtin_amdgcn_cvt_f32_fp8((int)a.shift_fp8[j], 0) * *a.shift_deq;
+            } else if (form == kAwq) {
+                sc = ldbf(a.scale, j);
+                sh = ldbf(a.shift, j);
             }
             const float xhat = (ldbf(xr, j) - mean) * rstd;
             y[e] = (xhat * (1.0f + sc)) + sh;
+            if (form == kAwq)
+                y[e] = y[e] * ldbf(a.inv_s, j);
             amax = fmaxf(amax, fabsf(y[e]));
         }
         const int E = mx_scale_exp(amax, 8);
@@ -528,10 +536,12 @@ hipError_t launch_mxfp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
         case kBcast: return launch_mxfp8_rows<kBcast>(a, rs, s);
         case kPtok: return launch_mxfp8_rows<kPtok>(a, rs, s);
         case kTable: return launch_mxfp8_rows<kTable>(a, rs, s);
+        case kModFp8: return launch_mxfp8_rows<kModFp8>(a, rs, s);
+        case kAwq: return launch_mxfp8_rows<kAwq>(a, rs, s);
         default: return hipErrorInvalidValue;
         }
     }
-    if (form != kNone && form != kBcast && form != kPtok && form != kTable)
+    if (form < kNone || form > kAwq)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)std::min<int64_t>(a.rows, kMaxGrid));
     hipLaunchKernelGGL(k_mxfp8_block, grid, dim3(256), 0, s, a, form);

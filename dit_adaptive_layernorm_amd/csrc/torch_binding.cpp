@@ -404,6 +404,66 @@ py::tuple mxfp8_table(const Tensor& x, const Tensor& temb, const Tensor& table, 
     return py::make_tuple(o, s);
 }
 
+py::tuple mxfp8_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& shift_fp8,
+                       const Tensor& scale_deq, const Tensor& shift_deq, double eps,
+                       const OptT& out, const OptT& scales, const OptT& row_mean,
+                       const OptT& row_rstd)
+{
+    int64_t rows, dim;
+    check_x(x, rows, dim);
+    Tensor s = mx_scales(x, rows, dim, scales);
+    Tensor o = fp8_out(out, x);
+    dev(scale_fp8, "scale_fp8", at::kFloat8_e4m3fn, {dim});
+    dev(shift_fp8, "shift_fp8", at::kFloat8_e4m3fn, {dim});
+    check("alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16",
+          alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16(
+              ptr<const uint16_t>(x), ptr<const uint8_t>(scale_fp8), ptr<const uint8_t>(shift_fp8),
+              act(scale_deq, "scale_deq"), act(shift_deq, "shift_deq"), (float)eps, rows, dim,
+              ptr<uint8_t>(o), ptr<uint8_t>(s), opt_f32(row_mean, "row_mean", rows),
+              opt_f32(row_rstd, "row_rstd", rows), stream()));
+    return py::make_tuple(o, s);
+}
+
+py::tuple awq_mxfp8(const Tensor& x, const Tensor& scale, const Tensor& shift, const Tensor& inv_s,
+                    double eps, const OptT& out, const OptT& scales, const OptT& row_mean,
+                    const OptT& row_rstd)
+{
+    int64_t rows, dim;
+    check_x(x, rows, dim);
+    Tensor s = mx_scales(x, rows, dim, scales);
+    Tensor o = fp8_out(out, x);
+    dev(scale, "scale", at::kBFloat16, {dim});
+    dev(shift, "shift", at::kBFloat16, {dim});
+    dev(inv_s, "inv_s", at::kBFloat16, {dim});
+    check("alnp_awq_ada_layer_norm_quant_mxfp8_bf16",
+          alnp_awq_ada_layer_norm_quant_mxfp8_bf16(
+              ptr<const uint16_t>(x), ptr<const uint16_t>(scale), ptr<const uint16_t>(shift),
+              ptr<const uint16_t>(inv_s), (float)eps, rows, dim, ptr<uint8_t>(o), ptr<uint8_t>(s),
+              opt_f32(row_mean, "row_mean", rows), opt_f32(row_rstd, "row_rstd", rows), stream()));
+    return py::make_tuple(o, s);
+}
+
+py::tuple mxfp4_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& shift_fp8,
+                       const Tensor& scale_deq, const Tensor& shift_deq, double eps,
+                       const OptT& packed, const OptT& scales, const OptT& row_mean,
+                       const OptT& row_rstd)
+{
+    int64_t rows, dim;
+    check_x(x, rows, dim);
+    Tensor s = mx_scales(x, rows, dim, scales);
+    Tensor p = packed ? *packed : at::empty({rows, dim / 2}, x.options().dtype(at::kByte));
+    dev(p, "packed", at::kByte, {rows, dim / 2});
+    dev(scale_fp8, "scale_fp8", at::kFloat8_e4m3fn, {dim});
+    dev(shift_fp8, "shift_fp8", at::kFloat8_e4m3fn, {dim});
+    check("alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16",
+          alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16(
+              ptr<const uint16_t>(x), ptr<const uint8_t>(scale_fp8), ptr<const uint8_t>(shift_fp8),
+              act(scale_deq, "scale_deq"), act(shift_deq, "shift_deq"), (float)eps, rows, dim,
+              ptr<uint8_t>(p), ptr<uint8_t>(s), opt_f32(row_mean, "row_mean", rows),
+              opt_f32(row_rstd, "row_rstd", rows), stream()));
+    return py::make_tuple(p, s);
+}
+
 py::tuple mxfp4(const Tensor& x, const c10::optional<Tensor>& scale,
                 const c10::optional<Tensor>& shift, double eps, const OptT& packed,
                 const OptT& scales, const OptT& row_mean, const OptT& row_rstd)
@@ -628,6 +688,21 @@ PYBIND11_MODULE(TORCH_EXTENSION_NAME, m)
           py::arg("x"), py::arg("scale"), py::arg("shift"), py::arg("eps") = 1e-5,
           py::arg("packed") = none, py::arg("scales") = none, py::arg("row_mean") = none,
           py::arg("row_rstd") = none, "Broadcast AdaLN -> bf16 stage -> MXFP4; scale, shift (dim,) bf16.");
+    m.def("ada_layer_norm_quant_mxfp8_modfp8_bf16", &mxfp8_modfp8, py::arg("x"),
+          py::arg("scale_fp8"), py::arg("shift_fp8"), py::arg("scale_deq"), py::arg("shift_deq"),
+          py::arg("eps") = 1e-5, py::arg("out") = none, py::arg("scales") = none,
+          py::arg("row_mean") = none, py::arg("row_rstd") = none,
+          "AdaLN with e4m3 (dim,) scale/shift and fp32 device dequantization scalars -> MXFP8.");
+    m.def("awq_ada_layer_norm_quant_mxfp8_bf16", &awq_mxfp8, py::arg("x"), py::arg("scale"),
+          py::arg("shift"), py::arg("inv_s"), py::arg("eps") = 1e-5, py::arg("out") = none,
+          py::arg("scales") = none, py::arg("row_mean") = none, py::arg("row_rstd") = none,
+          "Broadcast AdaLN -> per-channel inv_s (dim,) bf16 -> MXFP8.");
+    m.def("ada_layer_norm_quant_mxfp4_modfp8_bf16", &mxfp4_modfp8, py::arg("x"),
+          py::arg("scale_fp8"), py::arg("shift_fp8"), py::arg("scale_deq"), py::arg("shift_deq"),
+          py::arg("eps") = 1e-5, py::arg("packed") = none, py::arg("scales") = none,
+          py::arg("row_mean") = none, py::arg("row_rstd") = none,
+          "AdaLN with e4m3 (dim,) scale/shift and fp32 device dequantization scalars -> bf16 "
+          "stage -> MXFP4.");
     m.def("adaln_modulation6_bf16", &modulation6, py::arg("adaln_params"),
           py::arg("layer_modulation"), py::arg("out") = none,
           "fp32 (batch, seq, 6, dim) + fp32 (6, dim) -> six bf16 (batch, seq, dim).");

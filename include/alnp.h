@@ -288,7 +288,10 @@ int alnp_gated_residual_bf16(const uint16_t* residual, const uint16_t* gate,
  *   element = round_to_nearest_even(v / X), saturated at +-448 (E4M3) or
  *   +-6 (E2M1); amax ignores NaN.
  * MXFP8 quantizes the FP8 path's fp32 y (no act_scale: the block scales take
- * its place); MXFP4 quantizes the bf16-staged value of the FP4 entries.
+ * its place); MXFP4 quantizes the bf16-staged value of the FP4 entries.  The
+ * operand forms are those of the FP8 entries (LayerNorm, broadcast,
+ * per-token, table, modfp8, AWQ) for MXFP8, and of the FP4 entries
+ * (LayerNorm, broadcast, modfp8) for MXFP4, with the same operand arguments.
  *   out      (rows, dim) e4m3 codes (MXFP8); packed (rows, dim/2) (MXFP4)
  *   scales   (rows, dim/32) E8M0 bytes, row-major
  * dim must be a multiple of 32 (ALNP_ERR_DIM).  Codes for NaN elements are
@@ -312,6 +315,20 @@ int alnp_ada_layer_norm_quant_mxfp8_ptok_table_bf16(
     const uint16_t* x, const uint16_t* temb, const float* table, int64_t chunks,
     int64_t shift_idx, int64_t scale_idx, float eps, int64_t rows, int64_t dim, uint8_t* out,
     uint8_t* scales, float* row_mean, float* row_rstd, void* stream);
+/* modfp8 form: e4m3 (dim,) scale / shift times fp32 device dequantization
+ * scalars, as for alnp_ada_layer_norm_quant_fp8_modfp8_bf16. */
+int alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16(const uint16_t* x, const uint8_t* scale_fp8,
+                                                const uint8_t* shift_fp8, const float* scale_deq,
+                                                const float* shift_deq, float eps, int64_t rows,
+                                                int64_t dim, uint8_t* out, uint8_t* scales,
+                                                float* row_mean, float* row_rstd, void* stream);
+/* AWQ form: broadcast modulation, then y * inv_s[j] (bf16 (dim,)) before the
+ * block quantization, as for alnp_awq_ada_layer_norm_quant_fp8_bf16. */
+int alnp_awq_ada_layer_norm_quant_mxfp8_bf16(const uint16_t* x, const uint16_t* scale,
+                                             const uint16_t* shift, const uint16_t* inv_s,
+                                             float eps, int64_t rows, int64_t dim, uint8_t* out,
+                                             uint8_t* scales, float* row_mean, float* row_rstd,
+                                             void* stream);
 int alnp_layer_norm_no_affine_quant_mxfp4_bf16(const uint16_t* x, float eps,
                                                int64_t rows, int64_t dim, uint8_t* packed,
                                                uint8_t* scales, float* row_mean,
@@ -320,6 +337,13 @@ int alnp_ada_layer_norm_quant_mxfp4_bf16(const uint16_t* x, const uint16_t* scal
                                          const uint16_t* shift, float eps, int64_t rows,
                                          int64_t dim, uint8_t* packed, uint8_t* scales,
                                          float* row_mean, float* row_rstd, void* stream);
+/* modfp8 form, as for alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16,
+ * with row-major E8M0 scales. */
+int alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16(const uint16_t* x, const uint8_t* scale_fp8,
+                                                const uint8_t* shift_fp8, const float* scale_deq,
+                                                const float* shift_deq, float eps, int64_t rows,
+                                                int64_t dim, uint8_t* packed, uint8_t* scales,
+                                                float* row_mean, float* row_rstd, void* stream);
 /* Bytes of an MX scale buffer: rows * dim / 32; negative status otherwise. */
 int64_t alnp_mx_scale_size(int64_t rows, int64_t dim);
 

@@ -503,6 +503,18 @@ def adaln_mxfp4(x, scale=None, shift=None, eps=1e-5, want_b=False, threads=1):
     return packed, scales, mean, rstd, b
 
 
+def adaln_mxfp4_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, eps=1e-5, threads=1):
+    """modfp8 AdaLN -> bf16 stage -> MXFP4: the MX block rule applied to the
+    modfp8 FP4 path's bf16-staged values.  Returns (packed, scales, mean, rstd,
+    b)."""
+    _, _, mean, rstd, b = adaln_fp4_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, eps,
+                                           want_b=True, threads=threads)
+    rows, dim = b.shape
+    codes, scales = mx_block_quant(b, fp4=True)
+    return (fp4_pack(codes).reshape(rows, dim // 2), scales.reshape(rows, dim // 32), mean, rstd,
+            b)
+
+
 def adaln_mxfp8(x, scale=None, shift=None, eps=1e-5, want_y=False, threads=1):
     """LN (None operands), broadcast ((dim,)) or per-token ((rows, dim)) AdaLN ->
     MXFP8.  Returns (out (rows, dim) e4m3, scales (rows, dim/32), mean, rstd, y)."""
@@ -526,6 +538,33 @@ def adaln_mxfp8(x, scale=None, shift=None, eps=1e-5, want_y=False, threads=1):
                               _rowptr(rstd, r0, 1), _rowptr(y, r0, dim))
     _parallel(rows, threads, run)
     return out, scales, mean, rstd, y
+
+
+def _mxfp8_of(y):
+    rows, dim = y.shape
+    codes, scales = mx_block_quant(y, fp4=False)
+    return codes.reshape(rows, dim), scales.reshape(rows, dim // 32)
+
+
+def adaln_mxfp8_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, eps=1e-5, threads=1):
+    """modfp8 AdaLN -> MXFP8: the MX block rule applied to the modfp8 FP8 path's
+    fp32 y (which does not depend on act_scale).  Returns (out, scales, mean,
+    rstd, y)."""
+    _, mean, rstd, y = adaln_fp8_modfp8(x, scale_fp8, shift_fp8, scale_deq, shift_deq, 1.0, eps,
+                                        want_y=True, threads=threads)
+    out, scales = _mxfp8_of(y)
+    return out, scales, mean, rstd, y
+
+
+def awq_adaln_mxfp8(x, scale, shift, inv_s, eps=1e-5, threads=1):
+    """AWQ AdaLN -> MXFP8: the broadcast y times inv_s[j] (one fp32 product, the
+    value the FP8 AWQ path scales by 1 / act_scale), then the MX block rule.
+    Returns (out, scales, mean, rstd, smoothed y)."""
+    _, mean, rstd, y = awq_adaln_fp8(x, scale, shift, inv_s, 1.0, eps, want_y=True,
+                                     threads=threads)
+    smoothed = (y * bf16_to_f32(_c(inv_s, np.uint16))[None, :]).astype(np.float32)
+    out, scales = _mxfp8_of(smoothed)
+    return out, scales, mean, rstd, smoothed
 
 
 def adaln_mxfp8_table(x, temb, table, shift_idx, scale_idx, eps=1e-5, want_y=False, threads=1):

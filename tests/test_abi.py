@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 26
+    assert len(names) == 29
     for n in names:
         assert hasattr(L, n), n
     assert sorted(alnp.SIGNATURES) == names
@@ -217,6 +217,24 @@ def test_mx_validation(L):
     assert call(table=C + 2) == ALIGN
     assert call(dim=48) == DIM
     assert call(x=None, temb=None, table=None, chunks=0, rows=0, out=None, sc=None) == OK
+    # modfp8 and AWQ forms: their operands are required and aligned.
+    m8 = L.alnp_ada_layer_norm_quant_mxfp8_modfp8_bf16
+
+    def mcall(x=A, sf=B, hf=B + 64, sd=C, hd=C + 4, eps=1e-5, rows=4, dim=64, out=A, sc=D):
+        return m8(x, sf, hf, sd, hd, eps, rows, dim, out, sc, None, None, None)
+    assert mcall(sf=None) == NULL
+    assert mcall(hd=None) == NULL
+    assert mcall(sd=C + 2) == ALIGN
+    assert mcall(dim=48) == DIM
+    assert mcall(eps=float("nan")) == ARG
+    aw = L.alnp_awq_ada_layer_norm_quant_mxfp8_bf16
+    assert aw(A, B, C, None, 1e-5, 4, 64, A, D, None, None, None) == NULL
+    assert aw(A, B, C, D + 1, 1e-5, 4, 64, A, D, None, None, None) == ALIGN
+    assert aw(A, B, C, D, 1e-5, 4, 48, A, D, None, None, None) == DIM
+    m4 = L.alnp_ada_layer_norm_quant_mxfp4_modfp8_bf16
+    assert m4(A, B, B + 64, C, None, 1e-5, 4, 64, B, C, None, None, None) == NULL
+    assert m4(A, B, B + 64, C, C + 4, 1e-5, 4, 80, B, C, None, None, None) == DIM
+    assert m4(None, None, None, None, None, 1e-5, 0, 64, None, None, None, None, None) == OK
     assert L.alnp_mx_scale_size(4096, 3072) == 4096 * 96
     assert L.alnp_mx_scale_size(4, 48) == DIM
     assert alnp.mx_scale_size(2, 64) == 4

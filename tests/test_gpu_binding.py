@@ -57,6 +57,11 @@ def cases():
             dev_bf16(tb["x"]), dev_bf16(tb["temb"]), dev_f32(tb["table"]), 4, 2),
         "layer_norm_no_affine_quant_mxfp4_bf16": (x4,),
         "ada_layer_norm_quant_mxfp4_bf16": (xb, dev_bf16(bc["scale"]), dev_bf16(bc["shift"])),
+        "ada_layer_norm_quant_mxfp8_modfp8_bf16": (xb, e4m3(DIM, 11), e4m3(DIM, 12), s_deq, h_deq),
+        "awq_ada_layer_norm_quant_mxfp8_bf16": (
+            xb, dev_bf16(bc["scale"]), dev_bf16(bc["shift"]),
+            (1.0 + 0.1 * torch.randn(DIM, device="cuda")).bfloat16()),
+        "ada_layer_norm_quant_mxfp4_modfp8_bf16": (xb, e4m3(DIM, 13), e4m3(DIM, 14), s_deq, h_deq),
         "adaln_modulation6_bf16": (dev_f32(m6["params"]), dev_f32(m6["mod"])),
         "gated_residual_bf16": (x, dev_bf16(f8["scale"]), dev_bf16(f8["shift"])),
         "rms_norm_modulate_seg_bf16": (

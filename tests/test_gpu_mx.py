@@ -1,7 +1,8 @@
 """Parity of the MX producers (MXFP8 and MXFP4, E8M0 scale per 32 elements)
 with the oracle through the C ABI: LN / broadcast / per-token / table forms at small
-and ragged shapes (row and fallback kernels), full-size workloads on sampled
-rows, unaligned input, constant rows.
+and ragged shapes (row and fallback kernels), the modfp8 and AWQ forms
+(MXFP8) and modfp8 (MXFP4) likewise, full-size workloads on sampled rows,
+unaligned input, constant rows.
 
 Codes follow the README's validation policy as elsewhere (>= 99.9% equal, the
 rest within one step).  A block scale may differ by one only where the
@@ -222,3 +223,106 @@ def test_row_statistics(orc):
     r4 = torch.empty_like(rstd)
     alnp.layer_norm_no_affine_quant_mxfp4_bf16(dev_bf16(d["x"]), row_mean=m4, row_rstd=r4)
     assert_stats_close(m4.cpu().numpy(), r4.cpu().numpy(), rm, rr)
+
+
+# ---- modfp8 and AWQ operand forms ------------------------------------------------------
+
+def _e4m3_codes(f32):
+    return torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _fp8(u8):
+    return torch.from_numpy(np.ascontiguousarray(u8)).cuda().view(torch.float8_e4m3fn)
+
+
+def _scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def _variant_inputs(rows, dim, seed):
+    d = inputs.make("bcast", rows=rows, dim=dim, seed=seed)
+    d["scale_fp8"] = _e4m3_codes(inputs.normal_f32((dim,), 0.3, seed, 9))
+    d["shift_fp8"] = _e4m3_codes(inputs.normal_f32((dim,), 0.3, seed, 10))
+    d["inv_s"] = inputs.to_bf16_bits(np.abs(inputs.normal_f32((dim,), 0.5, seed, 11)) + 0.5)
+    return d
+
+
+VARIANT_SHAPES = [(1, 2048), (7, 3072), (63, 1536), (9, 5376), (5, 32), (4, 96), (2, 12000),
+                  (2, 32800), (1, 40000)]
+
+
+def _mxfp8_modfp8(d, sdeq, hdeq, x=None):
+    x = dev_bf16(d["x"]) if x is None else x
+    o, s = alnp.ada_layer_norm_quant_mxfp8_modfp8_bf16(
+        x, _fp8(d["scale_fp8"]), _fp8(d["shift_fp8"]), _scalar(sdeq), _scalar(hdeq))
+    return host_u8(o), host_u8(s)
+
+
+def _mxfp8_awq(d, x=None):
+    x = dev_bf16(d["x"]) if x is None else x
+    o, s = alnp.awq_ada_layer_norm_quant_mxfp8_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]),
+                                                    dev_bf16(d["inv_s"]))
+    return host_u8(o), host_u8(s)
+
+
+def _mxfp4_modfp8(d, sdeq, hdeq, x=None):
+    x = dev_bf16(d["x"]) if x is None else x
+    p, s = alnp.ada_layer_norm_quant_mxfp4_modfp8_bf16(
+        x, _fp8(d["scale_fp8"]), _fp8(d["shift_fp8"]), _scalar(sdeq), _scalar(hdeq))
+    return unpack_e2m1(host_u8(p)), host_u8(s)
+
+
+@pytest.mark.parametrize("rows,dim", VARIANT_SHAPES)
+def test_mx_modfp8_and_awq_shapes(orc, rows, dim):
+    print(f"mx variants rows={rows} dim={dim}", flush=True)
+    d = _variant_inputs(rows, dim, rows + 19 * dim)
+    codes, scales = _mxfp8_modfp8(d, 0.75, 1.5)
+    rc, rs, _, _, y = orc.adaln_mxfp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5,
+                                             threads=8)
+    assert_mx_close(codes, scales, rc, rs, y, e4m3_ordinal, f"mxfp8 modfp8 {rows}x{dim}")
+    codes, scales = _mxfp8_awq(d)
+    rc, rs, _, _, ys = orc.awq_adaln_mxfp8(d["x"], d["scale"], d["shift"], d["inv_s"], threads=8)
+    assert_mx_close(codes, scales, rc, rs, ys, e4m3_ordinal, f"mxfp8 awq {rows}x{dim}")
+    codes, scales = _mxfp4_modfp8(d, 0.75, 1.5)
+    rp, rs, _, _, b = orc.adaln_mxfp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5,
+                                             threads=8)
+    assert_mx_close(codes, scales, unpack_e2m1(rp), rs, b, e2m1_ordinal, f"mxfp4 modfp8 {rows}x{dim}")
+
+
+def test_mx_variants_unaligned_use_fallback(orc):
+    rows, dim = 9, 3072
+    d = _variant_inputs(rows, dim, 61)
+    x = misaligned_like((rows, dim), torch.bfloat16)
+    x.copy_(dev_bf16(d["x"]))
+    codes, scales = _mxfp8_modfp8(d, 0.5, 2.0, x=x)
+    rc, rs, _, _, y = orc.adaln_mxfp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.5, 2.0)
+    assert_mx_close(codes, scales, rc, rs, y, e4m3_ordinal, "mxfp8 modfp8 unaligned")
+    codes, scales = _mxfp8_awq(d, x=x)
+    rc, rs, _, _, ys = orc.awq_adaln_mxfp8(d["x"], d["scale"], d["shift"], d["inv_s"])
+    assert_mx_close(codes, scales, rc, rs, ys, e4m3_ordinal, "mxfp8 awq unaligned")
+    codes, scales = _mxfp4_modfp8(d, 0.5, 2.0, x=x)
+    rp, rs, _, _, b = orc.adaln_mxfp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.5, 2.0)
+    assert_mx_close(codes, scales, unpack_e2m1(rp), rs, b, e2m1_ordinal, "mxfp4 modfp8 unaligned")
+
+
+def test_mx_variants_reduce_to_broadcast_bitwise():
+    # modfp8 with unit dequantization equals broadcast with the decoded values
+    # as bf16 operands (exact), and AWQ with inv_s = 1 equals broadcast.
+    d = _variant_inputs(33, 3072, 62)
+    x = dev_bf16(d["x"])
+    sc = _fp8(d["scale_fp8"]).float().bfloat16()
+    sh = _fp8(d["shift_fp8"]).float().bfloat16()
+    bo, bs = alnp.ada_layer_norm_quant_mxfp8_bf16(x, sc, sh)
+    mo, ms = alnp.ada_layer_norm_quant_mxfp8_modfp8_bf16(
+        x, _fp8(d["scale_fp8"]), _fp8(d["shift_fp8"]), _scalar(1.0), _scalar(1.0))
+    assert np.array_equal(host_u8(mo), host_u8(bo)) and np.array_equal(host_u8(ms), host_u8(bs))
+    bp, bps = alnp.ada_layer_norm_quant_mxfp4_bf16(x, sc, sh)
+    mp, mps = alnp.ada_layer_norm_quant_mxfp4_modfp8_bf16(
+        x, _fp8(d["scale_fp8"]), _fp8(d["shift_fp8"]), _scalar(1.0), _scalar(1.0))
+    assert np.array_equal(host_u8(mp), host_u8(bp)) and np.array_equal(host_u8(mps), host_u8(bps))
+    ones = torch.ones(3072, dtype=torch.bfloat16, device="cuda")
+    s_dev, h_dev = dev_bf16(d["scale"]), dev_bf16(d["shift"])
+    bo, bs = alnp.ada_layer_norm_quant_mxfp8_bf16(x, s_dev, h_dev)
+    ao, as_ = alnp.awq_ada_layer_norm_quant_mxfp8_bf16(x, s_dev, h_dev, ones)
+    assert np.array_equal(host_u8(ao), host_u8(bo)) and np.array_equal(host_u8(as_), host_u8(bs))

@@ -5,6 +5,7 @@ exponent, closed forms at the scale's edges, torch's float8_e4m3fn conversion
 for MXFP8 elements, invariance under power-of-two scaling, and composition
 with the pinned FP4/FP8 paths for what gets quantized."""
 import numpy as np
+import pytest
 import torch
 
 from dit_adaptive_layernorm_amd import inputs
@@ -153,3 +154,53 @@ def test_mxfp8_table_quantizes_the_table_paths_y(orc):
     codes, scales = orc.mx_block_quant(y, fp4=False)
     assert np.array_equal(codes.reshape(out.shape), out) and np.array_equal(scales.reshape(s.shape), s)
 
+
+
+def _e4m3_operands(dim, seed):
+    """Finite e4m3 codes (NaN codes excluded) for (dim,) modfp8 operands."""
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 256, dim).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    return codes
+
+
+def _bf16_of_e4m3(orc, codes, deq):
+    # Every e4m3 value times a power of two is exact in bf16.
+    return orc.f32_to_bf16((orc.e4m3_decode(codes) * np.float64(deq)).astype(np.float32))
+
+
+@pytest.mark.parametrize("deq", [(1.0, 1.0), (0.5, 0.25), (4.0, 0.125)])
+def test_mxfp8_modfp8_is_broadcast_with_the_decoded_operands(orc, deq):
+    d = inputs.make("bcast", rows=11, dim=512, seed=50)
+    sf, hf = _e4m3_operands(512, 51), _e4m3_operands(512, 52)
+    got = orc.adaln_mxfp8_modfp8(d["x"], sf, hf, deq[0], deq[1])
+    ref = orc.adaln_mxfp8(d["x"], _bf16_of_e4m3(orc, sf, deq[0]), _bf16_of_e4m3(orc, hf, deq[1]),
+                          want_y=True)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8))
+
+
+@pytest.mark.parametrize("deq", [(1.0, 1.0), (0.5, 2.0)])
+def test_mxfp4_modfp8_is_broadcast_with_the_decoded_operands(orc, deq):
+    d = inputs.make("bcast", rows=9, dim=256, seed=53)
+    sf, hf = _e4m3_operands(256, 54), _e4m3_operands(256, 55)
+    got = orc.adaln_mxfp4_modfp8(d["x"], sf, hf, deq[0], deq[1])
+    ref = orc.adaln_mxfp4(d["x"], _bf16_of_e4m3(orc, sf, deq[0]), _bf16_of_e4m3(orc, hf, deq[1]),
+                          want_b=True)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8))
+
+
+def test_mxfp8_awq_identity_and_power_of_two_smoothing(orc):
+    d = inputs.make("bcast", rows=8, dim=512, seed=56)
+    one = np.full(512, 0x3F80, np.uint16)                       # bf16 1.0
+    got = orc.awq_adaln_mxfp8(d["x"], d["scale"], d["shift"], one)
+    ref = orc.adaln_mxfp8(d["x"], d["scale"], d["shift"], want_y=True)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8))
+    # inv_s = 2^k in every channel: the same element codes, scales moved by k
+    # (away from the E8M0 clamp).
+    for k in (-3, 2):
+        pk = np.full(512, (127 + k) << 7, np.uint16)            # bf16 2^k
+        o, s, _, _, _ = orc.awq_adaln_mxfp8(d["x"], d["scale"], d["shift"], pk)
+        assert np.array_equal(o, ref[0]) and np.array_equal(s.astype(int), ref[1].astype(int) + k)
