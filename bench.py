@@ -455,11 +455,20 @@ def cpu_baseline(d, nbytes):
                               threads=threads)
         passes.append(time.perf_counter() - t)
     dt = float(np.median(passes))
+    # One thread on the first quarter of the rows (same per-row work).
+    part = max(1, rows // 4)
+    t = time.perf_counter()
+    oracle.adaln_fp8_ptok(d["x"][:part], d["scale"][:part], d["shift"][:part], d["act_scale"],
+                          d["eps"], threads=1)
+    dt1 = time.perf_counter() - t
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
             "sample": f"the whole per-token 2520x3072 workload ({rows} rows), rows split "
                       f"over {threads} threads; median of {len(passes)} passes "
-                      f"({sum(passes) * threads:.1f} s of CPU time), wall clock"}
+                      f"({sum(passes) * threads:.1f} s of CPU time), wall clock",
+            "single_thread": {"value": round(nbytes * part / rows / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"rows 0..{part} of the same workload on one thread, "
+                                        f"one pass ({dt1:.2f} s)"}}
 
 
 # ---- main -------------------------------------------------------------------------------------
