@@ -27,6 +27,7 @@ functions without "swizzled" write plain row-major (rows, dim // 16) scales
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import sysconfig
 import types
@@ -124,18 +125,34 @@ _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 _cur_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
+_device_index = _cur_device if _cur_device is not None else torch.cuda.current_device
+
+
 def _stream() -> int:
-    if _raw_stream is not None and _cur_device is not None:
-        return _raw_stream(_cur_device())
+    if _raw_stream is not None:
+        return _raw_stream(_device_index())
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_call_device(fn):
+    """Run `fn` on the device of its first argument, a GPU tensor, as torch's
+    own operators do: switch the current device only when it differs.  Every
+    other tensor of the call must be on that device (checked by _dev)."""
+    @functools.wraps(fn)
+    def run(first, *args, **kwargs):
+        if isinstance(first, torch.Tensor) and first.is_cuda and first.get_device() != _device_index():
+            with torch.cuda.device(first.device):
+                return fn(first, *args, **kwargs)
+        return fn(first, *args, **kwargs)
+    return run
+
+
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
-    """Device pointer of a contiguous GPU tensor of the given dtype (and
-    shape); raises with the reason otherwise."""
+    """Device pointer of a contiguous tensor of the given dtype (and shape) on
+    the call's GPU (the current device); raises with the reason otherwise."""
     try:
-        if (t.dtype is dtype and t.is_cuda and t.is_contiguous()
-                and (shape is None or t.shape == shape)):
+        if (t.dtype is dtype and t.is_cuda and t.get_device() == _device_index()
+                and t.is_contiguous() and (shape is None or t.shape == shape)):
             return t.data_ptr()
     except AttributeError:
         pass
@@ -143,6 +160,9 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU")
+    if t.get_device() != _device_index():
+        raise ValueError(f"{name} must be on cuda:{_device_index()}, the device of the call, "
+                         f"got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -654,6 +674,10 @@ _COMPILED_NAMES = (
     "ada_layer_norm_quant_mxfp4_modfp8_bf16",
     "adaln_modulation6_bf16", "gated_residual_bf16", "rms_norm_modulate_seg_bf16",
 )
+
+# Each ctypes function runs on the device of its first tensor.
+for _n in _COMPILED_NAMES:
+    globals()[_n] = _on_call_device(globals()[_n])
 
 # The ctypes functions, whichever binding is public.
 ctypes_api = types.SimpleNamespace(**{_n: globals()[_n] for _n in _COMPILED_NAMES})

@@ -1,14 +1,17 @@
 // torch_binding.cpp -- the package's functions as compiled code.
 //
-// Every function takes torch tensors, checks them (GPU, dtype, shape,
+// Every function takes torch tensors, runs on the device of its first tensor
+// (as torch's own operators do), checks them (GPU, that device, dtype, shape,
 // contiguity), allocates the outputs it is not given, and calls the C ABI of
-// libalnp.so (include/alnp.h) on torch's current stream of the current
-// device: the same steps as the ctypes functions in __init__.py, without the
+// libalnp.so (include/alnp.h) on torch's current stream of that device: the
+// same steps as the ctypes functions in __init__.py, without the
 // Python-level checks and ctypes marshalling that cost about 3 us per call.
 // Nothing here computes; errors raise the same Python exception types as
 // those functions (ValueError, TypeError, and the package's AlnpError for a
 // status from the library).
 #include <torch/extension.h>
+#include <c10/core/DeviceGuard.h>
+#include <c10/hip/HIPFunctions.h>
 #include <c10/hip/HIPStream.h>
 
 #include <string>
@@ -48,11 +51,29 @@ std::string shape_str(at::IntArrayRef s)
     return r + ")";
 }
 
-// GPU, dtype, (shape,) contiguity, in that order, as the ctypes functions.
-void dev(const Tensor& t, const char* name, at::ScalarType dt)
+// The device a call runs on: that of its first tensor.  A guard on it makes
+// it the current device for the call (a no-op when it already is).
+c10::optional<c10::Device> call_device(const Tensor& t)
+{
+    return t.is_cuda() ? c10::make_optional(t.device()) : c10::nullopt;
+}
+
+// A GPU tensor on the call's device (the current one), else ValueError.
+void on_call_device(const Tensor& t, const char* name)
 {
     if (!t.is_cuda())
         throw py::value_error(std::string(name) + " must be on the GPU");
+    const int cur = c10::hip::current_device();
+    if (t.get_device() != cur)
+        throw py::value_error(std::string(name) + " must be on cuda:" + std::to_string(cur) +
+                              ", the device of the call, got " + t.device().str());
+}
+
+// GPU, device, dtype, (shape,) contiguity, in that order, as the ctypes
+// functions.
+void dev(const Tensor& t, const char* name, at::ScalarType dt)
+{
+    on_call_device(t, name);
     if (t.scalar_type() != dt)
         throw py::type_error(std::string(name) + " must be " + c10::toString(dt) + ", got " +
                              c10::toString(t.scalar_type()));
@@ -62,8 +83,7 @@ void dev(const Tensor& t, const char* name, at::ScalarType dt)
 
 void dev(const Tensor& t, const char* name, at::ScalarType dt, at::IntArrayRef shape)
 {
-    if (!t.is_cuda())
-        throw py::value_error(std::string(name) + " must be on the GPU");
+    on_call_device(t, name);
     if (t.scalar_type() != dt)
         throw py::type_error(std::string(name) + " must be " + c10::toString(dt) + ", got " +
                              c10::toString(t.scalar_type()));
@@ -118,6 +138,7 @@ Tensor ada_fp8_bcast(const Tensor& x, const Tensor& scale, const Tensor& shift,
                      const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                      const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -135,6 +156,7 @@ Tensor ada_fp8_ptok(const Tensor& x, const Tensor& scale, const Tensor& shift,
                     const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                     const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -152,6 +174,7 @@ Tensor ada_fp8_table(const Tensor& x, const Tensor& temb, const Tensor& table,
                      const Tensor& act_scale, int64_t shift_idx, int64_t scale_idx, double eps,
                      const OptT& out, const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (temb.dim() != 3)
@@ -172,6 +195,7 @@ Tensor ada_fp8_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& sh
                       const Tensor& scale_deq, const Tensor& shift_deq, const Tensor& act_scale,
                       double eps, const OptT& out, const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -190,6 +214,7 @@ Tensor awq_fp8(const Tensor& x, const Tensor& scale, const Tensor& shift, const 
                const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -207,6 +232,7 @@ Tensor awq_fp8(const Tensor& x, const Tensor& scale, const Tensor& shift, const 
 Tensor ln_fp8(const Tensor& x, const Tensor& act_scale, double eps, const OptT& out,
               const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -219,6 +245,7 @@ Tensor ln_fp8(const Tensor& x, const Tensor& act_scale, double eps, const OptT& 
 
 Tensor quant_fp8(const Tensor& v, const Tensor& act_scale, const OptT& out)
 {
+    const c10::OptionalDeviceGuard guard(call_device(v));
     dev(v, "v", at::kFloat);
     Tensor o = out ? *out : at::empty(v.sizes(), v.options().dtype(at::kFloat8_e4m3fn));
     dev(o, "out", at::kFloat8_e4m3fn, v.sizes());
@@ -273,6 +300,7 @@ std::pair<Tensor, Tensor> fp4_outputs(const Tensor& x, int64_t rows, int64_t dim
 py::tuple ln_nvfp4(const Tensor& x, double eps, const OptT& packed, const OptT& sf,
                    const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, false, true);
@@ -286,6 +314,7 @@ py::tuple ln_nvfp4(const Tensor& x, double eps, const OptT& packed, const OptT& 
 py::tuple ln_nvfp4_swizzled(const Tensor& x, double eps, const OptT& packed, const OptT& sf,
                             const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, true, false);
@@ -300,6 +329,7 @@ py::tuple ada_nvfp4(const Tensor& x, const Tensor& scale, const Tensor& shift, d
                     const OptT& packed, const OptT& sf, const OptT& row_mean, const OptT& row_rstd,
                     bool swizzled)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, swizzled, false);
@@ -318,6 +348,7 @@ py::tuple ada_nvfp4_swizzled_modfp8(const Tensor& x, const Tensor& scale_fp8,
                                     const Tensor& shift_deq, double eps, const OptT& packed,
                                     const OptT& sf, const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, true, false);
@@ -350,6 +381,7 @@ py::tuple mxfp8(const Tensor& x, const c10::optional<Tensor>& scale,
                 const c10::optional<Tensor>& shift, double eps, const OptT& out,
                 const OptT& scales, const OptT& row_mean, const OptT& row_rstd, int form)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -387,6 +419,7 @@ py::tuple mxfp8_table(const Tensor& x, const Tensor& temb, const Tensor& table, 
                       int64_t scale_idx, double eps, const OptT& out, const OptT& scales,
                       const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (temb.dim() != 3)
@@ -409,6 +442,7 @@ py::tuple mxfp8_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& s
                        const OptT& out, const OptT& scales, const OptT& row_mean,
                        const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -428,6 +462,7 @@ py::tuple awq_mxfp8(const Tensor& x, const Tensor& scale, const Tensor& shift, c
                     double eps, const OptT& out, const OptT& scales, const OptT& row_mean,
                     const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -448,6 +483,7 @@ py::tuple mxfp4_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& s
                        const OptT& packed, const OptT& scales, const OptT& row_mean,
                        const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -468,6 +504,7 @@ py::tuple mxfp4(const Tensor& x, const c10::optional<Tensor>& scale,
                 const c10::optional<Tensor>& shift, double eps, const OptT& packed,
                 const OptT& scales, const OptT& row_mean, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -495,6 +532,7 @@ py::tuple mxfp4(const Tensor& x, const c10::optional<Tensor>& scale,
 
 py::tuple modulation6(const Tensor& params, const Tensor& mod, const c10::optional<std::vector<Tensor>>& out)
 {
+    const c10::OptionalDeviceGuard guard(call_device(params));
     if (params.dim() != 4 || params.size(2) != 6)
         throw py::value_error("adaln_params must be (batch, seq, 6, dim)");
     const int64_t B = params.size(0), S = params.size(1), D = params.size(3);
@@ -523,6 +561,7 @@ py::tuple modulation6(const Tensor& params, const Tensor& mod, const c10::option
 
 Tensor gated_residual(const Tensor& residual, const Tensor& gate, const Tensor& proj, const OptT& out)
 {
+    const c10::OptionalDeviceGuard guard(call_device(residual));
     if (residual.dim() != 2)
         throw py::value_error("residual must be 2-D (rows, dim)");
     const int64_t rows = residual.size(0), dim = residual.size(1);
@@ -549,6 +588,7 @@ Tensor gated_residual(const Tensor& residual, const Tensor& gate, const Tensor& 
 Tensor rms_modulate(const Tensor& x, const OptT& weight, const Tensor& scale, const Tensor& shift,
                     const Tensor& seg, double eps, const OptT& out, const OptT& row_rstd)
 {
+    const c10::OptionalDeviceGuard guard(call_device(x));
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (scale.dim() != 2)

@@ -156,3 +156,19 @@ def test_misuse_raises_alike():
     small = torch.empty((7,), dtype=torch.uint8, device="cuda")
     e = _errors("layer_norm_no_affine_quant_nvfp4_swizzled_bf16", (x4,), {"sf_swizzled": small})
     assert type(e[0]) is type(e[1]) is ValueError and str(e[0]) == str(e[1]), e
+
+
+def test_tensor_off_the_call_device_is_rejected(monkeypatch):
+    """Every function runs on its first tensor's device and takes no tensor
+    from another.  With one GPU a second device cannot be made, so the ctypes
+    path is shown a call device of cuda:1: its cuda:0 tensors must then be
+    rejected (ValueError naming both devices) before anything is launched."""
+    args = cases()
+    res, gate, proj = args["gated_residual_bf16"]
+    before = res.clone()
+    monkeypatch.setattr(alnp, "_device_index", lambda: 1)
+    with pytest.raises(ValueError, match=r"must be on cuda:1, the device of the call, got cuda:0"):
+        alnp.ctypes_api.gated_residual_bf16(res, gate, proj, out=res)
+    monkeypatch.undo()
+    torch.cuda.synchronize()
+    assert torch.equal(res, before)
