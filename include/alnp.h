@@ -28,6 +28,12 @@
  *    (ALNP_ERR_ARG).  rows == 0 is a valid no-op.  If the launch itself
  *    fails, ALNP_ERR_LAUNCH is returned.  Device scalars (act_scale) are not
  *    inspected on the host.
+ *  - Devices: every pointer of a call must be memory of the GPU that is the
+ *    calling thread's current HIP device, and `stream` must belong to it;
+ *    the kernel is launched there.  The library does not inspect pointers to
+ *    find their device (that would cost microseconds per call), so this is
+ *    the caller's to ensure; the package's Python functions run each call on
+ *    the device of its first tensor and reject tensors from another.
  *  - Aliasing: outputs must not overlap inputs or each other.
  *  - Limits: rows (and batch * seq) <= 2^24 - 1; dim <= 2^24;
  *    alnp_quant_fp8_static_f32 takes n <= 2^31.
