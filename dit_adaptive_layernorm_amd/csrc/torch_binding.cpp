@@ -51,22 +51,39 @@ std::string shape_str(at::IntArrayRef s)
     return r + ")";
 }
 
-// The device a call runs on: that of its first tensor.  A guard on it makes
-// it the current device for the call (a no-op when it already is).
-c10::optional<c10::Device> call_device(const Tensor& t)
-{
-    return t.is_cuda() ? c10::make_optional(t.device()) : c10::nullopt;
-}
+// Index of the GPU the running call is on (set by CallDevice, read by the
+// tensor checks without asking the runtime again for every tensor).
+thread_local int t_call_device = -1;
 
-// A GPU tensor on the call's device (the current one), else ValueError.
+// The device a call runs on: that of its first tensor, as for torch's own
+// operators.  A guard makes it the current device for the call (nothing to
+// switch when it already is) and restores the previous one afterwards.
+class CallDevice {
+public:
+    explicit CallDevice(const Tensor& first)
+        : guard_(first.is_cuda() ? c10::make_optional(first.device()) : c10::nullopt),
+          saved_(t_call_device)
+    {
+        t_call_device = first.is_cuda() ? first.get_device() : c10::hip::current_device();
+    }
+    ~CallDevice() { t_call_device = saved_; }
+    CallDevice(const CallDevice&) = delete;
+    CallDevice& operator=(const CallDevice&) = delete;
+
+private:
+    c10::OptionalDeviceGuard guard_;
+    int saved_;
+};
+
+// A GPU tensor on the call's device, else ValueError.
 void on_call_device(const Tensor& t, const char* name)
 {
     if (!t.is_cuda())
         throw py::value_error(std::string(name) + " must be on the GPU");
-    const int cur = c10::hip::current_device();
-    if (t.get_device() != cur)
-        throw py::value_error(std::string(name) + " must be on cuda:" + std::to_string(cur) +
-                              ", the device of the call, got " + t.device().str());
+    if (t.get_device() != t_call_device)
+        throw py::value_error(std::string(name) + " must be on cuda:" +
+                              std::to_string(t_call_device) + ", the device of the call, got " +
+                              t.device().str());
 }
 
 // GPU, device, dtype, (shape,) contiguity, in that order, as the ctypes
@@ -138,7 +155,7 @@ Tensor ada_fp8_bcast(const Tensor& x, const Tensor& scale, const Tensor& shift,
                      const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                      const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -156,7 +173,7 @@ Tensor ada_fp8_ptok(const Tensor& x, const Tensor& scale, const Tensor& shift,
                     const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                     const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -174,7 +191,7 @@ Tensor ada_fp8_table(const Tensor& x, const Tensor& temb, const Tensor& table,
                      const Tensor& act_scale, int64_t shift_idx, int64_t scale_idx, double eps,
                      const OptT& out, const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (temb.dim() != 3)
@@ -195,7 +212,7 @@ Tensor ada_fp8_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& sh
                       const Tensor& scale_deq, const Tensor& shift_deq, const Tensor& act_scale,
                       double eps, const OptT& out, const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -214,7 +231,7 @@ Tensor awq_fp8(const Tensor& x, const Tensor& scale, const Tensor& shift, const 
                const Tensor& act_scale, double eps, const OptT& out, const OptT& row_mean,
                const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -232,7 +249,7 @@ Tensor awq_fp8(const Tensor& x, const Tensor& scale, const Tensor& shift, const 
 Tensor ln_fp8(const Tensor& x, const Tensor& act_scale, double eps, const OptT& out,
               const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor o = fp8_out(out, x);
@@ -245,7 +262,7 @@ Tensor ln_fp8(const Tensor& x, const Tensor& act_scale, double eps, const OptT& 
 
 Tensor quant_fp8(const Tensor& v, const Tensor& act_scale, const OptT& out)
 {
-    const c10::OptionalDeviceGuard guard(call_device(v));
+    const CallDevice call(v);
     dev(v, "v", at::kFloat);
     Tensor o = out ? *out : at::empty(v.sizes(), v.options().dtype(at::kFloat8_e4m3fn));
     dev(o, "out", at::kFloat8_e4m3fn, v.sizes());
@@ -300,7 +317,7 @@ std::pair<Tensor, Tensor> fp4_outputs(const Tensor& x, int64_t rows, int64_t dim
 py::tuple ln_nvfp4(const Tensor& x, double eps, const OptT& packed, const OptT& sf,
                    const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, false, true);
@@ -314,7 +331,7 @@ py::tuple ln_nvfp4(const Tensor& x, double eps, const OptT& packed, const OptT& 
 py::tuple ln_nvfp4_swizzled(const Tensor& x, double eps, const OptT& packed, const OptT& sf,
                             const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, true, false);
@@ -329,7 +346,7 @@ py::tuple ada_nvfp4(const Tensor& x, const Tensor& scale, const Tensor& shift, d
                     const OptT& packed, const OptT& sf, const OptT& row_mean, const OptT& row_rstd,
                     bool swizzled)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, swizzled, false);
@@ -348,7 +365,7 @@ py::tuple ada_nvfp4_swizzled_modfp8(const Tensor& x, const Tensor& scale_fp8,
                                     const Tensor& shift_deq, double eps, const OptT& packed,
                                     const OptT& sf, const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     auto [p, s] = fp4_outputs(x, rows, dim, packed, sf, true, false);
@@ -381,7 +398,7 @@ py::tuple mxfp8(const Tensor& x, const c10::optional<Tensor>& scale,
                 const c10::optional<Tensor>& shift, double eps, const OptT& out,
                 const OptT& scales, const OptT& row_mean, const OptT& row_rstd, int form)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -419,7 +436,7 @@ py::tuple mxfp8_table(const Tensor& x, const Tensor& temb, const Tensor& table, 
                       int64_t scale_idx, double eps, const OptT& out, const OptT& scales,
                       const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (temb.dim() != 3)
@@ -442,7 +459,7 @@ py::tuple mxfp8_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& s
                        const OptT& out, const OptT& scales, const OptT& row_mean,
                        const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -462,7 +479,7 @@ py::tuple awq_mxfp8(const Tensor& x, const Tensor& scale, const Tensor& shift, c
                     double eps, const OptT& out, const OptT& scales, const OptT& row_mean,
                     const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -483,7 +500,7 @@ py::tuple mxfp4_modfp8(const Tensor& x, const Tensor& scale_fp8, const Tensor& s
                        const OptT& packed, const OptT& scales, const OptT& row_mean,
                        const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -504,7 +521,7 @@ py::tuple mxfp4(const Tensor& x, const c10::optional<Tensor>& scale,
                 const c10::optional<Tensor>& shift, double eps, const OptT& packed,
                 const OptT& scales, const OptT& row_mean, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     Tensor s = mx_scales(x, rows, dim, scales);
@@ -532,7 +549,7 @@ py::tuple mxfp4(const Tensor& x, const c10::optional<Tensor>& scale,
 
 py::tuple modulation6(const Tensor& params, const Tensor& mod, const c10::optional<std::vector<Tensor>>& out)
 {
-    const c10::OptionalDeviceGuard guard(call_device(params));
+    const CallDevice call(params);
     if (params.dim() != 4 || params.size(2) != 6)
         throw py::value_error("adaln_params must be (batch, seq, 6, dim)");
     const int64_t B = params.size(0), S = params.size(1), D = params.size(3);
@@ -561,7 +578,7 @@ py::tuple modulation6(const Tensor& params, const Tensor& mod, const c10::option
 
 Tensor gated_residual(const Tensor& residual, const Tensor& gate, const Tensor& proj, const OptT& out)
 {
-    const c10::OptionalDeviceGuard guard(call_device(residual));
+    const CallDevice call(residual);
     if (residual.dim() != 2)
         throw py::value_error("residual must be 2-D (rows, dim)");
     const int64_t rows = residual.size(0), dim = residual.size(1);
@@ -588,7 +605,7 @@ Tensor gated_residual(const Tensor& residual, const Tensor& gate, const Tensor& 
 Tensor rms_modulate(const Tensor& x, const OptT& weight, const Tensor& scale, const Tensor& shift,
                     const Tensor& seg, double eps, const OptT& out, const OptT& row_rstd)
 {
-    const c10::OptionalDeviceGuard guard(call_device(x));
+    const CallDevice call(x);
     int64_t rows, dim;
     check_x(x, rows, dim);
     if (scale.dim() != 2)
