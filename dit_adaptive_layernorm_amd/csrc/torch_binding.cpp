@@ -64,7 +64,7 @@ public:
         : guard_(first.is_cuda() ? c10::make_optional(first.device()) : c10::nullopt),
           saved_(t_call_device)
     {
-        t_call_device = first.is_cuda() ? first.get_device() : c10::hip::current_device();
+        t_call_device = first.is_cuda() ? first.get_device() : -1;
     }
     ~CallDevice() { t_call_device = saved_; }
     CallDevice(const CallDevice&) = delete;
@@ -75,12 +75,14 @@ private:
     int saved_;
 };
 
-// A GPU tensor on the call's device, else ValueError.
+// A GPU tensor on the call's device, else ValueError.  A first tensor that
+// is not on the GPU leaves no call device (-1); the call then fails on that
+// tensor's own check, which every function makes.
 void on_call_device(const Tensor& t, const char* name)
 {
     if (!t.is_cuda())
         throw py::value_error(std::string(name) + " must be on the GPU");
-    if (t.get_device() != t_call_device)
+    if (t_call_device >= 0 && t.get_device() != t_call_device)
         throw py::value_error(std::string(name) + " must be on cuda:" +
                               std::to_string(t_call_device) + ", the device of the call, got " +
                               t.device().str());
