@@ -196,7 +196,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 // two rows instead of once per row.  The table loads (L2 hits) are issued
 // before the row loads so that the LDS fill does not wait behind them.
 constexpr int kTableRows = 2;     // rows per workgroup
-constexpr int kTableMaxDim = 8192; // 2 table rows * 8192 * 4 B = 64 KiB of LDS
+// LDS bound: 2 table rows * 8192 * 4 B = 64 KiB.  The row shapes of at most
+// four waves, which this kernel takes, end at dim 7168 (57344 bytes) anyway.
+constexpr int kTableMaxDim = 8192;
 // Up to this many rows the table form runs the rows kernel instead, which
 // holds each thread's table values in registers: with few rows resident,
 // registers are not what limits the kernel, and skipping the LDS staging and

@@ -83,6 +83,25 @@ def test_full_size_workloads(orc, name):
     assert np.allclose(rstd, 1 / np.sqrt(xf.var(1) + 1e-5), rtol=1e-5, atol=0)
 
 
+# From 513 rows the table form runs its LDS-staged kernel (two rows per
+# workgroup, both fp32 table rows in LDS) for rows of up to 4 waves.  Row
+# shapes of 1, 2 and 4 waves with 1 to 7 vectors per thread; 3080 has a
+# partial last vector slot; 7168 (2 waves x 7 vectors, 57344 bytes of tables
+# in LDS) is the largest dim it takes: 7176, 8192 and 8200 have 8-wave rows
+# and run the rows kernel.  601 rows: the last workgroup's second row lies
+# past the end.
+@pytest.mark.parametrize("dim", [512, 1152, 1536, 2048, 3080, 4096, 5376, 6144, 7168, 7176,
+                                 8192, 8200])
+def test_table_lds_kernel_dims(orc, dim):
+    rows = 601
+    d = inputs.make("table", rows=rows, dim=dim, seed=dim, shift_idx=4, scale_idx=1)
+    print(f"fp8 table rows={rows} dim={dim}", flush=True)
+    got, mean, rstd = run_gpu("table", d, rows, dim)
+    ref, rmean, rrstd = run_oracle(orc, "table", d)
+    assert_codes_close(got, ref, e4m3_ordinal, f"table {rows}x{dim}")
+    assert_stats_close(mean, rstd, rmean, rrstd)
+
+
 @pytest.mark.parametrize("kind", ["ln", "bcast", "ptok", "table"])
 def test_unaligned_pointers_use_fallback(orc, kind):
     rows, dim = 9, 3072

@@ -195,6 +195,18 @@ def test_mxfp8_table_batch_invariance_across_kernels():
         assert np.array_equal(o, full_o[r0:r0 + bs]) and np.array_equal(sc, full_s[r0:r0 + bs]), (r0, bs)
 
 
+@pytest.mark.parametrize("dim", [1536, 5376, 7168])
+def test_mxfp8_table_lds_kernel_dims(orc, dim):
+    """The MXFP8 table form's LDS-staged kernel (from 513 rows), up to the
+    largest dim it takes (7168: 2 waves x 7 vectors, 57344 bytes of tables
+    in LDS), with an odd row count."""
+    d = inputs.make("table", rows=601, dim=dim, seed=dim + 1, shift_idx=0, scale_idx=5)
+    print(f"mxfp8 table rows=601 dim={dim}", flush=True)
+    codes, scales = run_mxfp8("table", d)
+    rc, rs, ry = oracle_mxfp8(orc, "table", d)
+    assert_mx_close(codes, scales, rc, rs, ry, e4m3_ordinal, f"mxfp8 table 601x{dim}")
+
+
 def test_infinite_block_maximum(orc):
     # A huge broadcast scale overflows y (and its bf16 stage) to +-inf in some
     # blocks: the block maximum is infinite, E = 127, infinities saturate and
