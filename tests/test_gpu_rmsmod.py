@@ -151,6 +151,20 @@ def test_span_path_with_changing_segments(orc, weight, dim):
     check(orc, got, d, weight=weight, seg=seg, what=f"span path {rows}x{dim}")
 
 
+@pytest.mark.parametrize("dim", [2048, 3080, 8192, 16384, 32768])
+def test_span_path_row_shapes(orc, dim):
+    # The span kernel at row shapes the workload does not use: 2 waves x 2
+    # vectors (2048), a partial last vector slot (3080: 1 wave x 7), 8 waves
+    # (8192, 16384) and the longest register-resident rows (32768: 8 waves x
+    # 8 vectors).  4097 rows; sampled rows, the last span's lone row included.
+    rows = 4097
+    print(f"rmsmod span rows={rows} dim={dim}", flush=True)
+    d = inputs.make("rmsmod", rows=rows, dim=dim, seed=15 + dim, segments=3)
+    out, rstd = run_gpu(d)
+    sel = np.unique(np.concatenate([sample_rows(rows, 96, seed=dim), [1, rows - 2]]))
+    check(orc, (out[sel], rstd[sel]), d, rows_sel=sel, what=f"span path {rows}x{dim}")
+
+
 def test_span_and_row_kernels_agree():
     # The same rows through the span kernel (4100 rows) and the one-row kernel
     # (calls of fewer than 4096 rows): identical outputs and row statistics.
