@@ -1,9 +1,11 @@
 """Extents of the launch mapping, against the oracle through the C ABI: row
 counts past the 65535 workgroups one grid dimension holds (the row kernels
 then use a second grid dimension; the table form and the RMSNorm producer's
-span kernel hold two rows per workgroup), and rows of 2^20 elements, which go
-to the workgroup-per-row fallback.  Rows on both sides of each boundary are
-checked."""
+span kernel hold two rows per workgroup); token and row counts past 4 x 65535
+for the six-way producer and the residual gate, which map four per thread
+onto two grid dimensions and then need the third; and rows of 2^20 elements,
+which go to the workgroup-per-row fallback.  Rows on both sides of each
+boundary are checked."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +116,27 @@ def test_fp4_and_rmsmod_rows_of_2_pow_20(orc):
                                         torch.from_numpy(r["seg"]).cuda())
     ref = orc.rms_modulate_seg(r["x"], r["weight"], r["scale"], r["shift"], r["seg"])[0]
     assert np.mean(host_u16(o) == ref) >= 0.999
+
+
+# Six-way modulation and the residual gate give each thread four tokens
+# (rows) and spread the groups over (blockIdx.y, blockIdx.z): from 4 * 65535
+# = 262140 tokens the third grid dimension is used.  262147: a second z
+# slice holding one partial group.  Bit-exact, compared in full.
+def test_modulation6_tokens_past_two_grid_dimensions(orc):
+    B, S, D = 1, 262147, 16
+    print(f"mod6 B={B} S={S} D={D}", flush=True)
+    d = inputs.make("mod6", batch=B, seq=S, dim=D, seed=10)
+    outs = alnp.adaln_modulation6_bf16(dev_f32(d["params"]), dev_f32(d["mod"]))
+    got = np.stack([host_u16(o) for o in outs])
+    assert np.array_equal(got, orc.modulation6(d["params"], d["mod"]))
+
+
+@pytest.mark.parametrize("bcast", [False, True])
+def test_gated_residual_rows_past_two_grid_dimensions(orc, bcast):
+    rows, dim = 262147, 16
+    print(f"gated residual rows={rows} dim={dim} bcast={bcast}", flush=True)
+    res = inputs.normal_bf16((rows, dim), 1.0, 11, 1)
+    gate = inputs.normal_bf16((dim,) if bcast else (rows, dim), 0.5, 11, 2)
+    proj = inputs.normal_bf16((rows, dim), 2.0, 11, 3)
+    out = alnp.gated_residual_bf16(dev_bf16(res), dev_bf16(gate), dev_bf16(proj))
+    assert np.array_equal(host_u16(out), orc.gated_residual(res, gate, proj))
