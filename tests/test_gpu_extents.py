@@ -140,3 +140,24 @@ def test_gated_residual_rows_past_two_grid_dimensions(orc, bcast):
     proj = inputs.normal_bf16((rows, dim), 2.0, 11, 3)
     out = alnp.gated_residual_bf16(dev_bf16(res), dev_bf16(gate), dev_bf16(proj))
     assert np.array_equal(host_u16(out), orc.gated_residual(res, gate, proj))
+
+
+def test_standalone_quantizer_at_its_limit(orc):
+    """quant_fp8_static_f32 takes up to 2^31 values (one thread each, 2^23
+    workgroups): the values past 2^31 - 2^8 and a sample of the rest against
+    the oracle's encoder.  The input is drawn on the GPU (8 GiB)."""
+    n = 1 << 31
+    print(f"quant fp8 n={n}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    v = torch.randn(n, generator=g, device="cuda") * 4.0
+    a = act(0.025)
+    out = alnp.quant_fp8_static_f32(v, a)
+    rng = np.random.default_rng(12)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 4096), np.arange(n - 256, n), [0, 1]]))
+    it = torch.from_numpy(idx).cuda()
+    vs = v[it].cpu().numpy()
+    got = out.view(torch.uint8)[it].cpu().numpy()
+    del v, out
+    torch.cuda.empty_cache()
+    ref = orc.e4m3_encode_sat(vs * np.float32(1.0 / np.float32(0.025)))
+    assert np.array_equal(got, ref)
