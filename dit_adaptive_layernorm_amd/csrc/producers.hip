@@ -20,8 +20,11 @@
 namespace alnp {
 
 // MX: MXFP8 output, one E8M0 scale per 32 elements (the four vectors of a
-// lane quad) in place of the static act_scale.
-template <int VPT, int WAVES, int FORM, bool MX = false>
+// lane quad) in place of the static act_scale.  FULL: the row fills every
+// vector slot (dim / 8 == VPT * WAVES * 64, as for dim 2048 and 3072), so the
+// last slot needs no bounds check, zero fill or predicated stores; the
+// launcher picks it, and the arithmetic is the same.
+template <int VPT, int WAVES, int FORM, bool MX = false, bool FULL = false>
 __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 {
     __shared__ float red[32];  // two sets of per-wave partials
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         uint4 xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, v == VPT - 1);
+            xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, !FULL && v == VPT - 1);
 
         // Modulation operands, requested before the reductions.  Per-token
         // rows and temb chunks are streamed; (dim,) vectors are shared by
@@ -74,10 +77,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         if (FORM == kBcast || FORM == kAwq) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                scv[v] = ld_row<false>(a.scale, v * T + t, nvec, v == VPT - 1);
-                shv[v] = ld_row<false>(a.shift, v * T + t, nvec, v == VPT - 1);
+                scv[v] = ld_row<false>(a.scale, v * T + t, nvec, !FULL && v == VPT - 1);
+                shv[v] = ld_row<false>(a.shift, v * T + t, nvec, !FULL && v == VPT - 1);
                 if (FORM == kAwq)
-                    isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, v == VPT - 1);
+                    isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, !FULL && v == VPT - 1);
             }
         } else if (FORM == kPtok || FORM == kTable) {
             const uint16_t* scr = FORM == kPtok ? a.scale + row * dim
@@ -86,20 +89,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                                                 : a.temb + (row * a.chunks + a.shift_idx) * dim;
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                scv[v] = ld_row<true>(scr, v * T + t, nvec, v == VPT - 1);
-                shv[v] = ld_row<true>(shr, v * T + t, nvec, v == VPT - 1);
+                scv[v] = ld_row<true>(scr, v * T + t, nvec, !FULL && v == VPT - 1);
+                shv[v] = ld_row<true>(shr, v * T + t, nvec, !FULL && v == VPT - 1);
             }
         } else if (FORM == kModFp8) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
-                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, v == VPT - 1);
-                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, v == VPT - 1);
+                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
+                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
             }
         }
         const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
         const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
 
-        const bool tail_ok = (VPT - 1) * T + t < nvec;
+        const bool tail_ok = FULL || (VPT - 1) * T + t < nvec;
         float mean, rstd, d[VPT][8];
         row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
                        [&](float v, int k) { return group_sum(v, red + 16 * k, WAVES); }, d, mean,
@@ -207,7 +210,8 @@ constexpr int kTableMaxDim = 8192;
 // row statistics in the same order, so the switch changes no bits.
 constexpr int64_t kTableLdsMinRows = 513;
 
-template <int VPT, int WAVES, int R = kTableRows, bool MX = false>
+// FULL as for k_adaln_fp8_rows.
+template <int VPT, int WAVES, int R = kTableRows, bool MX = false, bool FULL = false>
 __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args a)
 {
     extern __shared__ float4 tab[];   // [0, dim/4): scale row, [dim/4, dim/2): shift row
@@ -244,11 +248,11 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     uint4 xv[VPT], scv[VPT], shv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-        xv[v] = ld_row<true>(xr, v * T + t, nvec, v == VPT - 1);
+        xv[v] = ld_row<true>(xr, v * T + t, nvec, !FULL && v == VPT - 1);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        scv[v] = ld_row<true>(scr, v * T + t, nvec, v == VPT - 1);
-        shv[v] = ld_row<true>(shr, v * T + t, nvec, v == VPT - 1);
+        scv[v] = ld_row<true>(scr, v * T + t, nvec, !FULL && v == VPT - 1);
+        shv[v] = ld_row<true>(shr, v * T + t, nvec, !FULL && v == VPT - 1);
     }
 
 #pragma unroll
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
 
     // Row statistics over the row's WAVES waves (the barriers also publish
     // the LDS table).
-    const bool tail_ok = (VPT - 1) * T + t < nvec;
+    const bool tail_ok = FULL || (VPT - 1) * T + t < nvec;
     float mean, rstd, d[VPT][8];
     row_stats<VPT>(xv, tail_ok, a.inv_dim, a.eps,
                    [&](float v, int k) { return subgroup_sum(v, red[k], rr * WAVES, WAVES); }, d,
@@ -449,6 +453,13 @@ template <int FORM>
 static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid(a.rows);
+    if ((a.dim >> 3) == rs.vpt * rs.threads) {
+#define ALNP_LAUNCH(V, W) \
+    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, false, true>), grid, dim3(W * 64), 0, s, a)
+        ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+        return hipGetLastError();
+    }
 #define ALNP_LAUNCH(V, W) \
     hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM>), grid, dim3(W * 64), 0, s, a)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)
@@ -461,8 +472,13 @@ static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
 template <int V, int W>
 static void launch_table_lds_shape(const Fp8Args& a, dim3 grid, size_t lds, hipStream_t s)
 {
-    if constexpr (W <= 4)
-        hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W>), grid, dim3(kTableRows * W * 64), lds, s, a);
+    if constexpr (W <= 4) {
+        if ((a.dim >> 3) == V * W * 64)
+            hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W, kTableRows, false, true>), grid,
+                               dim3(kTableRows * W * 64), lds, s, a);
+        else
+            hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W>), grid, dim3(kTableRows * W * 64), lds, s, a);
+    }
 }
 
 static hipError_t launch_fp8_table_lds(const Fp8Args& a, RowShape rs, hipStream_t s)
@@ -503,6 +519,13 @@ template <int FORM>
 static hipError_t launch_mxfp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid(a.rows);
+    if ((a.dim >> 3) == rs.vpt * rs.threads) {
+#define ALNP_LAUNCH(V, W) \
+    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, true, true>), grid, dim3(W * 64), 0, s, a)
+        ALNP_SHAPE_CASES(ALNP_LAUNCH)
+#undef ALNP_LAUNCH
+        return hipGetLastError();
+    }
 #define ALNP_LAUNCH(V, W) \
     hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, true>), grid, dim3(W * 64), 0, s, a)
     ALNP_SHAPE_CASES(ALNP_LAUNCH)
@@ -513,9 +536,14 @@ static hipError_t launch_mxfp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s
 template <int V, int W>
 static void launch_table_lds_mx_shape(const Fp8Args& a, dim3 grid, size_t lds, hipStream_t s)
 {
-    if constexpr (W <= 4)
-        hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W, kTableRows, true>), grid,
-                           dim3(kTableRows * W * 64), lds, s, a);
+    if constexpr (W <= 4) {
+        if ((a.dim >> 3) == V * W * 64)
+            hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W, kTableRows, true, true>), grid,
+                               dim3(kTableRows * W * 64), lds, s, a);
+        else
+            hipLaunchKernelGGL((k_adaln_fp8_table_lds<V, W, kTableRows, true>), grid,
+                               dim3(kTableRows * W * 64), lds, s, a);
+    }
 }
 
 hipError_t launch_mxfp8(const Fp8Args& args, int form, bool fast, hipStream_t s)
