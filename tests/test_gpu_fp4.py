@@ -80,3 +80,23 @@ def test_batch_invariance_and_determinism():
             p, s = alnp.layer_norm_no_affine_quant_nvfp4_bf16(x[r0:r0 + bs])
             assert np.array_equal(host_u8(p), p1[r0:r0 + bs])
             assert np.array_equal(host_u8(s), s1[r0:r0 + bs])
+
+
+def test_zero_eps_constant_row(orc):
+    """eps = 0 and a constant row: xhat = 0 * inf is NaN at every element, the
+    staged block maximum ignores NaN and is 0, so every block scale is code 0
+    and every code 0 (the zero-scale rule), on both sides bit for bit; the
+    other rows as usual."""
+    rows, dim = 4, 3072
+    d = inputs.make("fp4", rows=rows, dim=dim, seed=22)
+    x = d["x"].copy()
+    x[2] = inputs.to_bf16_bits(np.full(dim, -1.25, np.float32))
+    packed, sf = alnp.layer_norm_no_affine_quant_nvfp4_bf16(dev_bf16(x), eps=0.0)
+    got = (host_u8(packed), host_u8(sf))
+    ref = orc.ln_fp4(x, eps=0.0)
+    assert np.all(got[0][2] == 0) and np.all(got[1][2] == 0)
+    assert np.array_equal(got[0][2], ref[0][2]) and np.array_equal(got[1][2], ref[1][2])
+    keep = [0, 1, 3]
+    assert_codes_close(unpack_e2m1(got[0][keep]), unpack_e2m1(ref[0][keep]), e2m1_ordinal,
+                       "eps 0 codes")
+    assert_codes_close(got[1][keep], ref[1][keep], e4m3_ordinal, "eps 0 scales")

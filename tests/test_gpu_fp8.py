@@ -195,3 +195,29 @@ def test_constant_and_saturating_rows(orc):
     got, _, _ = run_gpu("bcast", d, rows, dim)
     ref = orc.adaln_fp8_bcast(xb, scale, shift, 0.025)[0]
     assert np.array_equal(got, ref)
+
+
+def test_zero_eps_constant_rows(orc):
+    """eps = 0 is accepted: a constant row then has variance 0 and rstd
+    1/sqrt(0) = inf, so xhat = 0 * inf is NaN and every code of the row is a
+    NaN code (its sign is whatever the platform's default NaN carries, so
+    only NaN-ness is compared there); the other rows match the oracle with
+    eps = 0 to the usual tolerance, statistics included."""
+    rows, dim = 6, 3072
+    d = inputs.make("ptok", rows=rows, dim=dim, seed=21)
+    x = d["x"].copy()
+    x[[1, 4]] = inputs.to_bf16_bits(np.full((2, dim), 0.625, np.float32))
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    o = alnp.ada_layer_norm_quant_fp8_ptok_bf16(dev_bf16(x), dev_bf16(d["scale"]),
+                                                dev_bf16(d["shift"]), act(d["act_scale"]),
+                                                eps=0.0, row_mean=mean, row_rstd=rstd)
+    got = host_u8(o)
+    ref, rmean, rrstd = orc.adaln_fp8_ptok(x, d["scale"], d["shift"], d["act_scale"], eps=0.0)[:3]
+    const = np.zeros(rows, bool)
+    const[[1, 4]] = True
+    assert np.all((got[const] & 0x7F) == 0x7F) and np.all((ref[const] & 0x7F) == 0x7F)
+    assert_codes_close(got[~const], ref[~const], e4m3_ordinal, "eps 0")
+    assert np.all(np.isinf(rstd.cpu().numpy()[const])) and np.all(np.isinf(rrstd[const]))
+    assert_stats_close(mean.cpu().numpy()[~const], rstd.cpu().numpy()[~const], rmean[~const],
+                       rrstd[~const])

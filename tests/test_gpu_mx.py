@@ -338,3 +338,21 @@ def test_mx_variants_reduce_to_broadcast_bitwise():
     bo, bs = alnp.ada_layer_norm_quant_mxfp8_bf16(x, s_dev, h_dev)
     ao, as_ = alnp.awq_ada_layer_norm_quant_mxfp8_bf16(x, s_dev, h_dev, ones)
     assert np.array_equal(host_u8(ao), host_u8(bo)) and np.array_equal(host_u8(as_), host_u8(bs))
+
+
+def test_zero_eps_constant_row(orc):
+    """eps = 0 and a constant row: every y is NaN, the block maximum (NaN
+    ignored) is 0, the scale code is the smallest, and every element code is
+    a NaN code on both sides (the sign of a NaN is the platform's)."""
+    rows, dim = 3, 1024
+    d = inputs.make("ln", rows=rows, dim=dim, seed=23)
+    x = d["x"].copy()
+    x[1] = inputs.to_bf16_bits(np.full(dim, 2.5, np.float32))
+    o, s = alnp.layer_norm_no_affine_quant_mxfp8_bf16(dev_bf16(x), eps=0.0)
+    codes, scales = host_u8(o), host_u8(s)
+    r = orc.adaln_mxfp8(x, eps=0.0, want_y=True)
+    rc, rs, ry = r[0], r[1], r[4]
+    assert np.array_equal(scales[1], rs[1])
+    assert np.all((codes[1] & 0x7F) == 0x7F) and np.all((rc[1] & 0x7F) == 0x7F)
+    keep = [0, 2]
+    assert_mx_close(codes[keep], scales[keep], rc[keep], rs[keep], ry[keep], e4m3_ordinal, "eps 0")
