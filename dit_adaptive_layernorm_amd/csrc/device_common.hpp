@@ -82,10 +82,13 @@ __device__ __forceinline__ float sat448(float v)
 
 // Four floats (already in range) -> four e4m3 codes, element a in byte 0.
 // v_cvt_pk_fp8_f32 rounds to nearest even and writes the OCP e4m3 format on
-// gfx950.
+// gfx950.  Each convert writes one half of the word and keeps the other; the
+// two together write all of it, so the word they start from is a's own bits
+// (a register already held) rather than a zero the compiler would have to
+// materialize.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -131,7 +134,9 @@ __device__ __forceinline__ uint32_t e2m1_code(float v)
 __device__ __forceinline__ uint32_t pack_e2m1x8(float a, float b, float c, float d, float e,
                                                 float f, float g, float h)
 {
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    // The four converts write all four bytes: start from a's bits (see
+    // pack_e4m3x4).
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(a), a, b, 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c, d, 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e, f, 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, g, h, 1.0f, 3);
@@ -194,20 +199,22 @@ __device__ __forceinline__ float dpp(float v)
 
 // Sum over the 64 lanes; every lane gets the same bits.  DPP butterflies
 // inside each row of 16 lanes (xor 1, xor 2, half-mirror, mirror: each lane
-// adds the same two operands as its partner, so partners hold identical
-// sums), then the four row sums are combined in a fixed order from lanes 0,
-// 16, 32 and 48.
+// adds the same two operands as its partner, so every lane of a row ends
+// with the row's sum r), then two row broadcasts: rows 1 and 3 add the sums
+// of rows 0 and 2 (row_bcast:15, rows 0 and 2 add zero), then rows 2 and 3
+// add row 1's (row_bcast:31), so lane 63 holds (r3 + r2) + (r1 + r0), which
+// one readlane hands to every lane.  IEEE addition is commutative, so this
+// is bit for bit the (r0 + r1) + (r2 + r3) of four readlanes, in three
+// instructions instead of nine.
 __device__ __forceinline__ float wave_sum(float v)
 {
     v = v + dpp<0xB1>(v);    // quad_perm [1,0,3,2]
     v = v + dpp<0x4E>(v);    // quad_perm [2,3,0,1]
     v = v + dpp<0x141>(v);   // row_half_mirror
     v = v + dpp<0x140>(v);   // row_mirror
-    float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (a + b) + (c + d);
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Sum over the waves of a workgroup (nwaves <= 16), same bits in every

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
             const float m = bf16_lo(pack_bf16x2(absmax8(y), 0.f));
             const int E = mx_scale_exp(quad_max(m), 2);
             const float xs = __uint_as_float((uint32_t)(E + 127) << 23);
-            uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[0]), xs, 0);
+            uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w[0], __builtin_bit_cast(bf16x2, w[0]), xs, 0);
             word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[1]), xs, 1);
             word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[2]), xs, 2);
             word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[3]), xs, 3);
