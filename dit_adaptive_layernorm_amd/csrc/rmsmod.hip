@@ -11,13 +11,20 @@ namespace alnp {
 // One modulated pair: the bf16 RMSNorm outputs n of two elements (already
 // rounded, packed), their operands, and the bf16 results packed.  Each step
 // is an fp32 operation rounded to bf16: t = bf16(scale + 1), u = bf16(n * t),
-// y = bf16(u + shift).
+// y = bf16(u + shift).  The second form takes t already computed (bf16
+// values held exactly in fp32).
+__device__ __forceinline__ uint32_t modulate_t_bf16x2(uint32_t n, float t0, float t1, float sh0,
+                                                      float sh1)
+{
+    const uint32_t u = pack_bf16x2(bf16_lo(n) * t0, bf16_hi(n) * t1);
+    return pack_bf16x2(bf16_lo(u) + sh0, bf16_hi(u) + sh1);
+}
+
 __device__ __forceinline__ uint32_t modulate_bf16x2(uint32_t n, float sc0, float sc1, float sh0,
                                                     float sh1)
 {
     const uint32_t t = pack_bf16x2(sc0 + 1.0f, sc1 + 1.0f);
-    const uint32_t u = pack_bf16x2(bf16_lo(n) * bf16_lo(t), bf16_hi(n) * bf16_hi(t));
-    return pack_bf16x2(bf16_lo(u) + sh0, bf16_hi(u) + sh1);
+    return modulate_t_bf16x2(n, bf16_lo(t), bf16_hi(t), sh0, sh1);
 }
 
 // One workgroup per row, the row in registers (same shapes as the FP8
@@ -88,18 +95,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_rows(RmsArgs a)
         a.row_rstd[row] = rstd;
 }
 
-// Rows [g * span, g * span + span) of workgroup g, one after another, each
+// Rows [g * SPAN, g * SPAN + SPAN) of workgroup g, one after another, each
 // as in k_rms_mod_rows (same arithmetic and reduction order, so the same
 // bits).  Consecutive rows mostly share their segment, so the weight and the
 // segment's modulation rows are read once per span into registers and read
 // again only when the segment changes; re-reading them from L2 for every row
 // is what separates the one-row kernel from a plain copy of the activations.
-// The next row's x is requested before the current row is reduced.  The
-// span's table indices come in with one vector load (span <= 64), and the
-// two reduction slots alternate so that one row's partials are not
+// With the segment's scale row the kernel keeps t = bf16(scale + 1) as fp32
+// (exact), computed once per segment instead of once per row.  The next
+// row's x is requested, into the other half of a register pair, before the
+// current row is reduced; the loop is unrolled, so nothing is copied between
+// rows.  The span's table indices come in with one vector load (SPAN <= 64),
+// and the two reduction slots alternate so that one row's partials are not
 // overwritten before every wave has read them.
-template <int VPT, int WAVES, bool W>
-__global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a, int span)
+template <int VPT, int WAVES, bool W, int SPAN>
+__global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
 {
     __shared__ float red[2][16];
     constexpr int T = WAVES * 64;
@@ -107,59 +117,73 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a, int span
     const int t = threadIdx.x;
     const int dim = a.dim;
     const int nvec = dim >> 3;
-    const int64_t r0 = grid_row() * span;
+    const int64_t r0 = grid_row() * SPAN;
     if (r0 >= a.rows)
         return;  // whole workgroup
-    const int n = (int)min<int64_t>(span, a.rows - r0);
+    const int n = (int)min<int64_t>(SPAN, a.rows - r0);
     const bool tail_ok = (VPT - 1) * T + t < nvec;
     const int lane = t & (kWave - 1);
     const int32_t segv = lane < n ? a.seg[r0 + lane] : 0;
 
-    uint4 xv[VPT], wv[NW], scv[VPT], shv[VPT];
+    uint4 xv[2][VPT], wv[NW], shv[VPT];
+    float tv[VPT][8];
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-        xv[v] = ld_row<true>(a.x + r0 * dim, v * T + t, nvec, v == VPT - 1);
+        xv[0][v] = ld_row<true>(a.x + r0 * dim, v * T + t, nvec, v == VPT - 1);
     if (W) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
             wv[v] = ld_row<false>(a.weight, v * T + t, nvec, v == VPT - 1);
     }
-    int64_t cur = -1;  // segment whose rows scv / shv hold
-    for (int k = 0; k < n; ++k) {
+    int64_t cur = -1;  // segment whose rows tv / shv hold
+#pragma unroll
+    for (int k = 0; k < SPAN; ++k) {
+        if (k >= n)
+            break;  // whole workgroup
         const int64_t row = r0 + k;
         const int32_t sidx = __builtin_amdgcn_readlane(segv, k);
         const bool in_range = sidx >= 0 && sidx < a.segments;
         const int64_t srow = in_range ? sidx : 0;
         if (srow != cur) {
+            uint4 scv[VPT];
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
                 scv[v] = ld_row<false>(a.scale + srow * dim, v * T + t, nvec, v == VPT - 1);
                 shv[v] = ld_row<false>(a.shift + srow * dim, v * T + t, nvec, v == VPT - 1);
             }
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                float sc[8];
+                unpack8(scv[v], sc);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t tt = pack_bf16x2(sc[e] + 1.0f, sc[e + 1] + 1.0f);
+                    tv[v][e] = bf16_lo(tt);
+                    tv[v][e + 1] = bf16_hi(tt);
+                }
+            }
             cur = srow;
         }
-        const bool more = k + 1 < n;
-        uint4 xn[VPT];
-        if (more) {
+        const uint4(&x)[VPT] = xv[k & 1];
+        if (k + 1 < n) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v)
-                xn[v] = ld_row<true>(a.x + (row + 1) * dim, v * T + t, nvec, v == VPT - 1);
+                xv[(k + 1) & 1][v] = ld_row<true>(a.x + (row + 1) * dim, v * T + t, nvec, v == VPT - 1);
         }
         float q = 0.f;
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            q = sumsq_bf16x8(xv[v], q);
+            q = sumsq_bf16x8(x[v], q);
         const float rstd = rsqrt_refined(group_sum(q, red[k & 1], WAVES) * a.inv_dim + a.eps);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int i = v * T + t;
             if (v == VPT - 1 && !tail_ok)
                 continue;
-            float f[8], w8[8], sc[8], sh[8];
-            unpack8(xv[v], f);
+            float f[8], w8[8], sh[8];
+            unpack8(x[v], f);
             if (W)
                 unpack8(wv[v], w8);
-            unpack8(scv[v], sc);
             unpack8(shv[v], sh);
             uint32_t o[4];
 #pragma unroll
@@ -169,19 +193,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a, int span
                     n0 = n0 * w8[2 * e];
                     n1 = n1 * w8[2 * e + 1];
                 }
-                o[e] = modulate_bf16x2(pack_bf16x2(n0, n1), sc[2 * e], sc[2 * e + 1], sh[2 * e],
-                                       sh[2 * e + 1]);
+                o[e] = modulate_t_bf16x2(pack_bf16x2(n0, n1), tv[v][2 * e], tv[v][2 * e + 1],
+                                         sh[2 * e], sh[2 * e + 1]);
                 o[e] = in_range ? o[e] : 0x7FC07FC0u;
             }
             st_stream(a.out + row * dim + (int64_t)i * 8, make_uint4(o[0], o[1], o[2], o[3]));
         }
         if (t == 0 && a.row_rstd)
             a.row_rstd[row] = rstd;
-        if (more) {
-#pragma unroll
-            for (int v = 0; v < VPT; ++v)
-                xv[v] = xn[v];
-        }
     }
 }
 
@@ -229,7 +248,7 @@ static hipError_t launch_rms_rows(const RmsArgs& a, RowShape rs, hipStream_t s)
     if (a.rows >= kRmsSpanMinRows) {
         const dim3 grid = row_grid((a.rows + kRmsSpan - 1) / kRmsSpan);
 #define ALNP_LAUNCH(V, WV) \
-    hipLaunchKernelGGL((k_rms_mod_span<V, WV, W>), grid, dim3(WV * 64), 0, s, a, kRmsSpan)
+    hipLaunchKernelGGL((k_rms_mod_span<V, WV, W, kRmsSpan>), grid, dim3(WV * 64), 0, s, a)
         ALNP_SHAPE_CASES(ALNP_LAUNCH)
 #undef ALNP_LAUNCH
         return hipGetLastError();
