@@ -1,13 +1,13 @@
 """Parity of the six-way modulation producer with the oracle, bit-exact,
 through the C ABI: small and ragged shapes (vector and scalar kernels), the
-full B1 S5070 D3072 workload on sampled tokens, and unaligned outputs."""
+full B1 S5070 D3072 workload on every token, and unaligned outputs."""
 import numpy as np
 import pytest
 import torch
 
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
-from parity import dev_f32, host_u16, misaligned_like, sample_rows
+from parity import dev_f32, host_u16, misaligned_like
 
 pytestmark = pytest.mark.gpu
 
@@ -29,10 +29,7 @@ def test_small_shapes(orc, B, S, D):
 def test_full_size_workload(orc):
     d = inputs.workload("modulation6_1x5070x3072")
     got = run_gpu(d["params"], d["mod"])
-    toks = sample_rows(5070, 200)
-    p = np.ascontiguousarray(d["params"][:, toks])
-    ref = orc.modulation6(p, d["mod"], threads=8)
-    assert np.array_equal(got[:, :, toks], ref)
+    assert np.array_equal(got, orc.modulation6(d["params"], d["mod"], threads=8))  # every token
 
 
 def test_unaligned_outputs(orc):

@@ -1,7 +1,7 @@
 """Parity of the MX producers (MXFP8 and MXFP4, E8M0 scale per 32 elements)
 with the oracle through the C ABI: LN / broadcast / per-token / table forms at small
 and ragged shapes (row and fallback kernels), the modfp8 and AWQ forms
-(MXFP8) and modfp8 (MXFP4) likewise, full-size workloads on sampled rows,
+(MXFP8) and modfp8 (MXFP4) likewise, full-size workloads on every row,
 unaligned input, constant rows.
 
 Codes follow the README's validation policy as elsewhere (>= 99.9% equal, the
@@ -17,7 +17,7 @@ import torch
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
 from parity import (assert_stats_close, dev_bf16, dev_f32, e2m1_ordinal, e4m3_ordinal, host_u8,
-                    misaligned_like, sample_rows, unpack_e2m1)
+                    misaligned_like, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,20 +112,18 @@ def test_mxfp4_shapes(orc, kind, rows, dim):
 
 
 @pytest.mark.parametrize("name,kind", [("ptok_fp8_2520x3072", "ptok"), ("table_fp8_2520x3072", "table")])
-def test_mxfp8_full_size_sampled(orc, name, kind):
+def test_mxfp8_full_size(orc, name, kind):
     d = inputs.workload(name)
     codes, scales = run_mxfp8(kind, d)
-    sel = sample_rows(2520, 160)
-    rc, rs, y = oracle_mxfp8(orc, kind, d, sel)
-    assert_mx_close(codes[sel], scales[sel], rc, rs, y, e4m3_ordinal, f"mxfp8 {kind} 2520x3072")
+    rc, rs, y = oracle_mxfp8(orc, kind, d)  # every row
+    assert_mx_close(codes, scales, rc, rs, y, e4m3_ordinal, f"mxfp8 {kind} 2520x3072")
 
 
-def test_mxfp4_full_size_sampled(orc):
+def test_mxfp4_full_size(orc):
     d = inputs.workload("ln_fp4_4096x3072")
     codes, scales = run_mxfp4("ln", d)
-    sel = sample_rows(4096, 160)
-    rc, rs, b = oracle_mxfp4(orc, "ln", d, sel)
-    assert_mx_close(codes[sel], scales[sel], rc, rs, b, e2m1_ordinal, "mxfp4 ln 4096x3072")
+    rc, rs, b = oracle_mxfp4(orc, "ln", d)  # every row
+    assert_mx_close(codes, scales, rc, rs, b, e2m1_ordinal, "mxfp4 ln 4096x3072")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])

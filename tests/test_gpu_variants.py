@@ -1,6 +1,6 @@
 """Parity of the FP8 variants (modfp8, AWQ) and the FP4 variants (AdaLN->FP4,
 128x4 tiled scales) with the oracle, through the C ABI: small and ragged
-shapes (fast and fallback kernels), a full Wan-size shape on sampled rows,
+shapes (fast and fallback kernels), full Wan-size shapes on every row,
 every finite e4m3 operand code, and the tiled layout's padding rules."""
 import numpy as np
 import pytest
@@ -9,7 +9,7 @@ import torch
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
 from parity import (act, assert_codes_close, assert_stats_close, dev_bf16, e2m1_ordinal,
-                    e4m3_ordinal, host_u8, misaligned_like, sample_rows, unpack_e2m1)
+                    e4m3_ordinal, host_u8, misaligned_like, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,14 +74,13 @@ def test_modfp8_every_finite_operand_code(orc):
         assert_codes_close(got, ref, e4m3_ordinal, f"modfp8 codes deq {sdeq}/{hdeq}")
 
 
-def test_modfp8_full_size_sampled(orc):
+def test_modfp8_full_size(orc):
     d = modfp8_inputs(2520, 3072, 32)
     got, m, r = run_modfp8(d, 1.0, 1.0)
-    sel = sample_rows(2520, 128)
-    ref, rm, rr, _ = orc.adaln_fp8_modfp8(np.ascontiguousarray(d["x"][sel]), d["scale_fp8"],
-                                          d["shift_fp8"], 1.0, 1.0, 0.025, threads=8)
-    assert_codes_close(got[sel], ref, e4m3_ordinal, "modfp8 2520x3072")
-    assert_stats_close(m[sel], r[sel], rm, rr)
+    ref, rm, rr, _ = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 1.0, 1.0, 0.025,
+                                          threads=8)  # every row
+    assert_codes_close(got, ref, e4m3_ordinal, "modfp8 2520x3072")
+    assert_stats_close(m, r, rm, rr)
 
 
 def test_modfp8_unaligned_fallback(orc):
@@ -268,15 +267,14 @@ def test_adaln_fp4_modfp8_unit_dequant_equals_broadcast_bitwise():
     assert np.array_equal(gp, host_u8(p2)) and np.array_equal(gs, host_u8(s2))
 
 
-def test_adaln_fp4_modfp8_full_size_sampled(orc):
+def test_adaln_fp4_modfp8_full_size(orc):
     rows, dim = 4096, 3072
     d = modfp8_inputs(rows, dim, seed=39)
     gp, gs = run_fp4_modfp8(d, 0.5, 2.0)
-    sel = sample_rows(rows, 128)
-    rp, rs, _, _, _ = orc.adaln_fp4_modfp8(np.ascontiguousarray(d["x"][sel]), d["scale_fp8"],
-                                           d["shift_fp8"], 0.5, 2.0, threads=8)
-    pos = swizzled_positions(orc, rows, dim // 16)[sel]
-    fp4_check(gp[sel], gs[pos], rp, rs, "fp4 modfp8 4096x3072")
+    rp, rs, _, _, _ = orc.adaln_fp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.5, 2.0,
+                                           threads=8)  # every row
+    pos = swizzled_positions(orc, rows, dim // 16)
+    fp4_check(gp, gs[pos], rp, rs, "fp4 modfp8 4096x3072")
 
 
 def test_adaln_fp4_modfp8_unaligned_fallback(orc):
@@ -298,14 +296,12 @@ def test_adaln_fp4_zero_modulation_equals_ln_fp4_bitwise():
     assert np.array_equal(host_u8(p1), host_u8(p2)) and np.array_equal(host_u8(s1), host_u8(s2))
 
 
-def test_adaln_fp4_full_size_sampled(orc):
+def test_adaln_fp4_full_size(orc):
     d = inputs.make("bcast", rows=4096, dim=3072, seed=36)
     packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(dev_bf16(d["x"]), dev_bf16(d["scale"]),
                                                       dev_bf16(d["shift"]))
-    sel = sample_rows(4096, 128)
-    rp, rs, _, _, _ = orc.adaln_fp4(np.ascontiguousarray(d["x"][sel]), d["scale"], d["shift"],
-                                    threads=8)
-    fp4_check(host_u8(packed)[sel], host_u8(sf)[sel], rp, rs, "adaln fp4 4096x3072")
+    rp, rs, _, _, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"], threads=8)  # every row
+    fp4_check(host_u8(packed), host_u8(sf), rp, rs, "adaln fp4 4096x3072")
 
 
 def test_adaln_fp4_unaligned_fallback(orc):
