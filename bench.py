@@ -10,8 +10,10 @@ step.  Launches are replayed from a HIP graph (the pages' graph method:
 several launches per graph, time / launches).
 
 The other producers (broadcast and table FP8, LN -> FP8, LN -> FP4,
-six-way modulation) are timed the same way at their workload sizes and
-reported under "rows"; the headline JSON line is the per-token FP8 one.
+six-way modulation, RMSNorm modulation, and the MXFP8 / MXFP4 outputs) are
+timed the same way at their workload sizes and reported under "rows", each
+beside its memory-only floor; the headline JSON line is the per-token FP8
+one.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--only-headline] [--direct]
