@@ -39,8 +39,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_FOOTPRINT = 512 << 20     # 2x the Infinity Cache
-COPY_BYTES = 256 << 20         # plain copy used to scale the rocprofv3 byte counters
+# Plain copies used to scale the rocprofv3 byte counters: about the per-token
+# workload's bytes, 256 MiB, and about the six-way workload's bytes.
+COPY_SIZES = (54 << 20, 256 << 20, 560 << 20)
+COUNTER_MAX_STEPS = 20
 THOR_PTOK_US = 229.922         # pages: NVIDIA Thor, per-token M2520 D3072, raw op
+REPEATS = 5                    # timed windows per measurement; the median is reported
 
 
 def parse():
@@ -48,6 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--repeats", type=int, default=REPEATS,
+                   help="timed windows of --steps launches per measurement (median reported)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-headline", action="store_true",
                    help="time only the per-token FP8 producer")
@@ -61,10 +67,38 @@ def parse():
                    help="skip the small-shape launch-overhead table")
     p.add_argument("--no-floor", action="store_true",
                    help="skip timing the memory-only counterparts (libalnp_floor.so)")
+    p.add_argument("--counters", action="store_true",
+                   help="run under rocprofv3 counter collection (--pmc): warm mode only, at "
+                        "most %d steps, one timed window, no floors, copies, overhead table "
+                        "or CPU baseline" % COUNTER_MAX_STEPS)
     p.add_argument("--calibrate-copy", action="store_true",
-                   help="only run four plain device copies of 256 MiB (reference for "
-                        "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
+                   help="only run plain device copies of %s bytes (torch's copy and "
+                        "alnp_floor_copy, four each; the reference for scaling rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE) and exit" % "/".join(map(str, COPY_SIZES)))
+    p.add_argument("--floor-sweep", action="store_true",
+                   help="only time the per-token producer and memory-only access patterns over "
+                        "a range of row counts at dim 3072 and exit")
     return p.parse_args()
+
+
+def counter_guard(a, modes):
+    """Counter collection (rocprofv3 --pmc) serializes every dispatch and
+    samples counters around it.  One such run ended in a host segmentation
+    fault (exit 139) while timing cold mode: thousands of buffer sets, each
+    allocated and filled by its own device copies, then graphs of 1000
+    launches.  Only the short warm form has been run under counters since.
+    Returns an error message for anything else, or None."""
+    collecting = os.environ.get("ROCPROF_COUNTER_COLLECTION", "").strip().lower() in (
+        "1", "true", "yes", "on")
+    if collecting and not a.counters:
+        return "rocprofv3 counter collection is active: pass --counters"
+    if not a.counters:
+        return None
+    if "cold" in modes:
+        return "--counters takes --modes warm only (cold mode is not run under counters)"
+    if a.steps > COUNTER_MAX_STEPS:
+        return f"--counters takes at most {COUNTER_MAX_STEPS} steps"
+    return None
 
 
 # ---- workloads ----------------------------------------------------------------
@@ -110,6 +144,11 @@ def floor_lib():
     F.alnp_floor_rows.restype = ctypes.c_int
     F.alnp_floor_modulation6.argtypes = [vp, i64, ctypes.c_int, ctypes.POINTER(vp), vp]
     F.alnp_floor_modulation6.restype = ctypes.c_int
+    F.alnp_floor_rows_shape.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                                        ctypes.c_int, ctypes.c_int, vp]
+    F.alnp_floor_rows_shape.restype = ctypes.c_int
+    F.alnp_floor_copy.argtypes = [vp, vp, i64, vp]
+    F.alnp_floor_copy.restype = ctypes.c_int
     return F
 
 
@@ -284,59 +323,303 @@ class Producer:
             raise RuntimeError(f"{self.name} floor: status {st}")
 
 
+class HipEvents:
+    """Timing events without the system-scope fence.  A HIP event recorded
+    with default flags performs a system-scope release (L2 writeback and
+    invalidation) when it completes; inside a short timed window that cost
+    lands on the launches being timed.  Events created with
+    hipEventDisableSystemFence record the timestamp without it, which HIP
+    documents for events used only to measure time.  The events come from
+    the HIP runtime the process already loaded (torch's), so they share
+    its streams; the window's completion is waited for with a device
+    synchronize before the elapsed times are read."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        with open("/proc/self/maps") as fh:
+            paths = [l.split()[-1] for l in fh if "libamdhip64" in l and "/" in l]
+        if not paths:
+            raise RuntimeError("the HIP runtime is not loaded")
+        H = ctypes.CDLL(paths[0])
+        vp = ctypes.c_void_p
+        H.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        H.hipEventRecord.argtypes = [vp, vp]
+        H.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        H.hipEventDestroy.argtypes = [vp]
+        for f in (H.hipEventCreateWithFlags, H.hipEventRecord, H.hipEventElapsedTime,
+                  H.hipEventDestroy):
+            f.restype = ctypes.c_int
+        self.H = H
+
+    def new(self):
+        e = ctypes.c_void_p()
+        st = self.H.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {st}")
+        return e
+
+    def record(self, e, stream):
+        st = self.H.hipEventRecord(e, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord: {st}")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        st = self.H.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {st}")
+        return ms.value
+
+    def free(self, *evs):
+        for e in evs:
+            self.H.hipEventDestroy(e)
+
+    # -- graphs with event-record nodes --------------------------------------
+
+    def _graph_api(self):
+        H = self.H
+        if getattr(self, "_graphs_ready", False):
+            return H
+        vp, pvp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)
+        sigs = {"hipStreamBeginCapture": [vp, ctypes.c_int],
+                "hipStreamEndCapture": [vp, pvp],
+                "hipGraphCreate": [pvp, ctypes.c_uint],
+                "hipGraphAddChildGraphNode": [pvp, vp, pvp, ctypes.c_size_t, vp],
+                "hipGraphAddEventRecordNode": [pvp, vp, pvp, ctypes.c_size_t, vp],
+                "hipGraphInstantiate": [pvp, vp, vp, vp, ctypes.c_size_t],
+                "hipGraphLaunch": [vp, vp],
+                "hipGraphExecDestroy": [vp],
+                "hipGraphDestroy": [vp]}
+        for name, args in sigs.items():
+            fn = getattr(H, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        self._graphs_ready = True
+        return H
+
+    @staticmethod
+    def _ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: HIP error {st}")
+
+    def capture(self, stream, launch, idxs):
+        """A graph of launch(i, stream) for i in idxs, captured on `stream`
+        (a torch stream that nothing else uses meanwhile)."""
+        H = self._graph_api()
+        h = stream.cuda_stream
+        self._ok(H.hipStreamBeginCapture(h, 1), "hipStreamBeginCapture")   # thread-local mode
+        try:
+            for i in idxs:
+                launch(i, h)
+        finally:
+            g = ctypes.c_void_p()
+            st = H.hipStreamEndCapture(h, ctypes.byref(g))
+        self._ok(st, "hipStreamEndCapture")
+        return g
+
+    def window_graph(self, spacer, timed, tail, t0, t1):
+        """One executable graph: spacer -> record t0 -> timed -> record t1 ->
+        tail (each a captured graph, cloned into a child node).  The graph
+        launch's own start-up cost falls before the spacer, outside the
+        window between the two event nodes."""
+        H = self._graph_api()
+        top = ctypes.c_void_p()
+        self._ok(H.hipGraphCreate(ctypes.byref(top), 0), "hipGraphCreate")
+        prev = None
+        for kind, obj in (("child", spacer), ("event", t0), ("child", timed), ("event", t1),
+                          ("child", tail)):
+            node = ctypes.c_void_p()
+            deps, ndeps = (ctypes.byref(prev), 1) if prev is not None else (None, 0)
+            if kind == "child":
+                self._ok(H.hipGraphAddChildGraphNode(ctypes.byref(node), top, deps, ndeps, obj),
+                         "hipGraphAddChildGraphNode")
+            else:
+                self._ok(H.hipGraphAddEventRecordNode(ctypes.byref(node), top, deps, ndeps, obj),
+                         "hipGraphAddEventRecordNode")
+            prev = node
+        ex = ctypes.c_void_p()
+        self._ok(H.hipGraphInstantiate(ctypes.byref(ex), top, None, None, 0), "hipGraphInstantiate")
+        H.hipGraphDestroy(top)     # the child nodes hold copies of the parts
+        return ex
+
+    def free_captured(self, *graphs):
+        for g in graphs:
+            self._graph_api().hipGraphDestroy(g)
+
+    def launch_graph(self, ex, stream):
+        self._ok(self._graph_api().hipGraphLaunch(ex, stream.cuda_stream), "hipGraphLaunch")
+
+    def free_graph(self, ex):
+        self._graph_api().hipGraphExecDestroy(ex)
+
+
+_EVENTS = None
+
+
+def hip_events():
+    global _EVENTS
+    if _EVENTS is None:
+        _EVENTS = HipEvents()
+    return _EVENTS
+
+
 def sets_for(nbytes, cold):
     return max(2, math.ceil(COLD_FOOTPRINT / nbytes)) if cold else 1
 
 
-def time_producer(prod, steps, warmup, use_graph, torch, stream, floor=False):
-    """Average us per step over exactly `steps` launches on `stream` (a
-    dedicated stream, as a pipeline would use), measured with HIP events
-    recorded on that stream.  With a graph, the `steps` launches are captured
-    once and the graph is replayed once untimed (upload) before the timed
-    replay.  floor=True times the memory-only counterparts instead."""
+def _capture(torch, launch, idxs):
+    """A HIP graph of launch(i) for i in idxs, captured on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        hh = torch.cuda.current_stream().cuda_stream
+        for i in idxs:
+            launch(i, hh)
+    return g
+
+
+SPACER_MIN_LAUNCHES = 64
+SPACER_MS = 20.0       # minimum GPU time of the spacer before each window
+TAIL_LAUNCHES = 8      # launches after the closing event node of a timed window
+
+
+def spacer_length(sets, steps, launch_us=None):
+    """Launches of the untimed spacer before each timed window: whole
+    rotations over the buffer sets (so that every set the timed window
+    touches was last touched one full rotation earlier, with all the other
+    sets' bytes in between); at least as many launches as the window and
+    SPACER_MIN_LAUNCHES; and, given an estimate of one launch's time, at
+    least SPACER_MS of work.  The last rule puts every window past the
+    first ~10 ms of load, during which the per-launch time on these boxes
+    first rises by up to 6% and then settles (clock and power management);
+    a window then measures the settled rate whatever its length."""
+    n = max(steps, SPACER_MIN_LAUNCHES)
+    if launch_us:
+        n = max(n, math.ceil(SPACER_MS * 1000.0 / launch_us))
+    return sets * max(1, math.ceil(n / sets))
+
+
+def time_launches(torch, stream, launch, sets, steps, warmup, use_graph, repeats=REPEATS):
+    """Median, min and max microseconds per launch over `repeats` timed
+    windows of exactly `steps` launches each (launch i uses buffer set
+    i mod sets), measured with HIP events on `stream`, the stream the
+    launches run on (HipEvents: no system-scope fence).
+
+    Each window is preceded by an untimed spacer of whole rotations over
+    the sets and at least SPACER_MS of work (spacer_length): every set the
+    window touches has been evicted by the rotation through all the others,
+    and the GPU has been under steady load for a while when the window
+    opens.
+
+    With a graph (the default), each repeat is one executable graph: the
+    spacer, an event-record node, the `steps` timed launches, a second
+    event-record node and a short tail.  The cost of starting a graph
+    launch (several microseconds on this runtime, paid once per launch
+    however many kernels the graph holds) then falls before the spacer,
+    outside the window, which holds exactly the timed launches.  The
+    repeats' graphs are launched back to back, between two device
+    synchronizations, so the GPU does not idle between windows.  Without a
+    graph the launches are enqueued directly, the events recorded on the
+    stream."""
+    E = hip_events()
     h = stream.cuda_stream
-    launch = prod.launch_floor if floor else prod.launch
+    samples = []
     with torch.cuda.stream(stream):
         for i in range(warmup):
             launch(i, h)
         torch.cuda.synchronize()
-        g = None
-        if use_graph:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-                hh = torch.cuda.current_stream().cuda_stream
-                for i in range(steps):
-                    launch(i, hh)
-            g.replay()
-            torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        if use_graph:
-            g.replay()
-        else:
-            for i in range(steps):
-                launch(i, h)
-        t1.record(stream)
+        # Rough per-launch time from a short untimed burst, to size the spacer.
+        a, b = E.new(), E.new()
+        E.record(a, stream)
+        for i in range(16):
+            launch(i, h)
+        E.record(b, stream)
         torch.cuda.synchronize()
-    del g
-    return t0.elapsed_time(t1) * 1000.0 / steps
+        nspace = spacer_length(sets, steps, E.elapsed_ms(a, b) * 1000.0 / 16)
+        E.free(a, b)
+        if use_graph:
+            cap = torch.cuda.Stream()
+            parts = [E.capture(cap, launch, r) for r in
+                     (range(nspace), range(steps), range(steps, steps + TAIL_LAUNCHES))]
+            windows = []
+            for _ in range(repeats):
+                t0, t1 = E.new(), E.new()
+                windows.append((E.window_graph(*parts, t0, t1), t0, t1))
+            E.free_captured(*parts)
+            for ex, _, _ in windows:            # upload, untimed
+                E.launch_graph(ex, stream)
+            torch.cuda.synchronize()
+            for ex, _, _ in windows:            # back to back: the GPU never idles
+                E.launch_graph(ex, stream)
+            torch.cuda.synchronize()
+            for ex, t0, t1 in windows:
+                samples.append(E.elapsed_ms(t0, t1) * 1000.0 / steps)
+                E.free_graph(ex)
+                E.free(t0, t1)
+        else:
+            events = []
+            for _ in range(repeats):
+                t0, t1 = E.new(), E.new()
+                for i in range(nspace):
+                    launch(i, h)
+                E.record(t0, stream)
+                for i in range(steps):
+                    launch(i, h)
+                E.record(t1, stream)
+                events.append((t0, t1))
+            torch.cuda.synchronize()
+            for a, b in events:
+                samples.append(E.elapsed_ms(a, b) * 1000.0 / steps)
+                E.free(a, b)
+    us = sorted(samples)
+    return {"us": float(np.median(us)), "min": us[0], "max": us[-1]}
+
+
+def time_producer(prod, steps, warmup, use_graph, torch, stream, floor=False, repeats=REPEATS):
+    """time_launches over a producer's buffer sets; floor=True times the
+    memory-only counterparts on the same buffers instead."""
+    return time_launches(torch, stream, prod.launch_floor if floor else prod.launch, prod.sets,
+                         steps, warmup, use_graph, repeats)
+
+
+class CopyCeiling:
+    """A plain copy (libalnp_floor.so's alnp_floor_copy) moving `nbytes` in
+    total, half read and half written, over cold-rotated buffer sets: the
+    practical ceiling for a stream of that size."""
+
+    def __init__(self, nbytes, cold, torch, F):
+        half = max(16, (nbytes // 2) // 16 * 16)
+        self.nbytes = 2 * half
+        self.sets = sets_for(self.nbytes, cold)
+        self.bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+                      torch.empty(half, dtype=torch.uint8, device="cuda"))
+                     for _ in range(self.sets)]
+        self.F, self.half = F, half
+
+    def launch(self, i, stream):
+        src, dst = self.bufs[i % self.sets]
+        st = self.F.alnp_floor_copy(src.data_ptr(), dst.data_ptr(), self.half, stream)
+        if st != 0:
+            raise RuntimeError(f"copy: status {st}")
 
 
 # ---- launch overhead at small shapes ---------------------------------------------------
 
-def launch_overhead(torch, alnp, inputs, stream, calls=400, graph_launches=32, replays=50):
+def launch_overhead(torch, alnp, inputs, stream, calls=400, graph_launches=32, replays=50,
+                    repeats=REPEATS):
     """The pages' small-shape method (Benchmark Results, "Six-way modulation
     producer" and "NVIDIA Thor installed artifact"): per shape, the raw C ABI
     launched directly, the Python wrapper launched directly (A-B-B-A order),
     and a HIP graph of 32 launches replayed, time / 32.  Inputs stay the same
-    buffers (warm): these shapes are latency-bound."""
+    buffers (warm): these shapes are latency-bound.  Every case is built and
+    run once, untimed, before any is timed (first calls pay one-time costs),
+    and each figure is the median of `repeats` rounds over all cases."""
     dev = torch.device("cuda")
     bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
     L = alnp.lib()
-    cases = {}
     act = torch.tensor([0.025], dtype=torch.float32, device=dev)
+    cases = {}
     for name, kind, rows, dim in (("ptok_fp8_51x1536", "ptok", 51, 1536),
                                   ("table_fp8_51x1536", "table", 51, 1536),
                                   ("ptok_fp8_105x1152", "ptok", 105, 1152),
@@ -346,67 +629,96 @@ def launch_overhead(torch, alnp, inputs, stream, calls=400, graph_launches=32, r
             p, m = f32(d["params"]), f32(d["mod"])
             outs = [torch.empty((1, rows, dim), dtype=torch.bfloat16, device=dev) for _ in range(6)]
             arr = (ctypes.c_void_p * 6)(*[o.data_ptr() for o in outs])
-            raw = lambda h: L.alnp_adaln_modulation6_bf16(p.data_ptr(), m.data_ptr(), 1, rows, dim, arr, h)
-            wrap = lambda h: alnp.adaln_modulation6_bf16(p, m, out=outs)
+            raw = (lambda p, m, rows, dim, arr: lambda h: L.alnp_adaln_modulation6_bf16(
+                p.data_ptr(), m.data_ptr(), 1, rows, dim, arr, h))(p, m, rows, dim, arr)
+            wrap = (lambda p, m, outs: lambda h: alnp.adaln_modulation6_bf16(p, m, out=outs))(p, m, outs)
+            keep = (p, m, outs, arr)
         elif kind == "ptok":
             d = inputs.make("ptok", rows=rows, dim=dim)
             x, sc, sh = bf(d["x"]), bf(d["scale"]), bf(d["shift"])
             out = torch.empty((rows, dim), dtype=torch.float8_e4m3fn, device=dev)
-            raw = lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_bf16(
+            raw = (lambda x, sc, sh, out, rows, dim: lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_bf16(
                 x.data_ptr(), sc.data_ptr(), sh.data_ptr(), act.data_ptr(), 1e-5, rows, dim,
-                out.data_ptr(), None, None, h)
-            wrap = lambda h: alnp.ada_layer_norm_quant_fp8_ptok_bf16(x, sc, sh, act, out=out)
+                out.data_ptr(), None, None, h))(x, sc, sh, out, rows, dim)
+            wrap = (lambda x, sc, sh, out: lambda h: alnp.ada_layer_norm_quant_fp8_ptok_bf16(
+                x, sc, sh, act, out=out))(x, sc, sh, out)
+            keep = (x, sc, sh, out)
         else:
             d = inputs.make("table", rows=rows, dim=dim)
             x, te, tb = bf(d["x"]), bf(d["temb"]), f32(d["table"])
             out = torch.empty((rows, dim), dtype=torch.float8_e4m3fn, device=dev)
-            raw = lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(
+            raw = (lambda x, te, tb, out, rows, dim: lambda h: L.alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(
                 x.data_ptr(), te.data_ptr(), tb.data_ptr(), 6, 0, 1, act.data_ptr(), 1e-5, rows,
-                dim, out.data_ptr(), None, None, h)
-            wrap = lambda h: alnp.ada_layer_norm_quant_fp8_ptok_table_bf16(x, te, tb, act, 0, 1, out=out)
+                dim, out.data_ptr(), None, None, h))(x, te, tb, out, rows, dim)
+            wrap = (lambda x, te, tb, out: lambda h: alnp.ada_layer_norm_quant_fp8_ptok_table_bf16(
+                x, te, tb, act, 0, 1, out=out))(x, te, tb, out)
+            keep = (x, te, tb, out)
+        cases[name] = {"raw": raw, "wrap": wrap, "keep": keep}
 
-        def direct(fn):
-            with torch.cuda.stream(stream):
-                h = stream.cuda_stream
-                for _ in range(20):
-                    fn(h)
-                t0 = torch.cuda.Event(enable_timing=True)
-                t1 = torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                t0.record(stream)
-                for _ in range(calls):
-                    fn(h)
-                t1.record(stream)
-                torch.cuda.synchronize()
-            return t0.elapsed_time(t1) * 1000.0 / calls
+    E = hip_events()
 
-        def graphed(fn):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
-                with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-                    hh = torch.cuda.current_stream().cuda_stream
-                    for _ in range(graph_launches):
-                        fn(hh)
+    def elapsed(t0, t1):
+        ms = E.elapsed_ms(t0, t1)
+        E.free(t0, t1)
+        return ms
+
+    def direct(fn):
+        with torch.cuda.stream(stream):
+            h = stream.cuda_stream
+            for _ in range(20):
+                fn(h)
+            t0, t1 = E.new(), E.new()
+            torch.cuda.synchronize()
+            E.record(t0, stream)
+            for _ in range(calls):
+                fn(h)
+            E.record(t1, stream)
+            torch.cuda.synchronize()
+        return elapsed(t0, t1) * 1000.0 / calls
+
+    def graphed(g):
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            t0, t1 = E.new(), E.new()
+            E.record(t0, stream)
+            for _ in range(replays):
                 g.replay()
-                torch.cuda.synchronize()
-                t0 = torch.cuda.Event(enable_timing=True)
-                t1 = torch.cuda.Event(enable_timing=True)
-                t0.record(stream)
-                for _ in range(replays):
-                    g.replay()
-                t1.record(stream)
-                torch.cuda.synchronize()
-            return t0.elapsed_time(t1) * 1000.0 / (replays * graph_launches)
+            E.record(t1, stream)
+            torch.cuda.synchronize()
+        return elapsed(t0, t1) * 1000.0 / (replays * graph_launches)
 
-        a1, b1, b2, a2 = direct(raw), direct(wrap), direct(wrap), direct(raw)
-        ga, gb = graphed(raw), graphed(wrap)
-        nat, wr = (a1 + a2) / 2, (b1 + b2) / 2
-        cases[name] = {"native_us": round(nat, 3), "wrapper_us": round(wr, 3),
-                       "graph_native_us": round(ga, 3), "graph_wrapper_us": round(gb, 3),
-                       "wrapper_over_native": round(wr / nat, 3)}
-        print(f"# overhead {name}: native {nat:.3f} us, wrapper {wr:.3f} us, graph native "
-              f"{ga:.3f} us, graph wrapper {gb:.3f} us", file=sys.stderr, flush=True)
-    return cases
+    # One untimed pass over every case, both call paths, then the graphs.
+    with torch.cuda.stream(stream):
+        for c in cases.values():
+            for _ in range(50):
+                c["raw"](stream.cuda_stream)
+                c["wrap"](stream.cuda_stream)
+        torch.cuda.synchronize()
+    for c in cases.values():
+        with torch.cuda.stream(stream):
+            c["graph_raw"] = _capture(torch, lambda i, h, f=c["raw"]: f(h), range(graph_launches))
+            c["graph_wrap"] = _capture(torch, lambda i, h, f=c["wrap"]: f(h), range(graph_launches))
+    samples = {n: {"nat": [], "wr": [], "ga": [], "gb": []} for n in cases}
+    for _ in range(repeats):
+        for name, c in cases.items():
+            a1, b1, b2, a2 = direct(c["raw"]), direct(c["wrap"]), direct(c["wrap"]), direct(c["raw"])
+            samples[name]["nat"].append((a1 + a2) / 2)
+            samples[name]["wr"].append((b1 + b2) / 2)
+            samples[name]["ga"].append(graphed(c["graph_raw"]))
+            samples[name]["gb"].append(graphed(c["graph_wrap"]))
+    out = {}
+    for name, sm in samples.items():
+        med = {k: float(np.median(v)) for k, v in sm.items()}
+        ratios = [w / n for w, n in zip(sm["wr"], sm["nat"])]
+        out[name] = {"native_us": round(med["nat"], 3), "wrapper_us": round(med["wr"], 3),
+                     "graph_native_us": round(med["ga"], 3), "graph_wrapper_us": round(med["gb"], 3),
+                     "wrapper_over_native": round(float(np.median(ratios)), 3),
+                     "wrapper_over_native_range": [round(min(ratios), 3), round(max(ratios), 3)]}
+        print(f"# overhead {name}: native {med['nat']:.3f} us, wrapper {med['wr']:.3f} us, graph "
+              f"native {med['ga']:.3f} us, graph wrapper {med['gb']:.3f} us (median of {repeats})",
+              file=sys.stderr, flush=True)
+    return out
 
 
 # ---- counters from rocprofv3 (profiles/) --------------------------------------------
@@ -475,12 +787,93 @@ def cpu_baseline(d, nbytes):
 
 # ---- main -------------------------------------------------------------------------------------
 
+def rounded(t):
+    """A time_launches record rounded for the JSON line."""
+    return {"us_per_call": round(t["us"], 3), "us_min": round(t["min"], 3),
+            "us_max": round(t["max"], 3)}
+
+
+def calibrate_copy(torch, F):
+    """Four plain copies of each size in COPY_SIZES, first torch's device copy,
+    then alnp_floor_copy (distinct kernels and grid sizes in the counter
+    output), for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    for nbytes in COPY_SIZES:
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        if F is not None:
+            for _ in range(4):
+                assert F.alnp_floor_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                         torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps({"calibrate_copy_bytes": list(COPY_SIZES), "copies_each": 4,
+                      "kernels": ["torch copy_", "k_floor_copy"] if F is not None else
+                      ["torch copy_"]}))
+
+
+SWEEP_ROWS = (315, 630, 1260, 2520, 5040, 10080, 20160)
+SWEEP_SHAPES = ((2, 3), (1, 6), (4, 2), (8, 1))
+
+
+def floor_sweep(torch, alnp, inputs, F, stream, steps, warmup, use_graph, repeats):
+    """The per-token producer beside its memory-only pattern and a plain copy
+    of the same bytes, over row counts at dim 3072, cold, with a least-squares
+    line time = intercept + bytes / slope for each; then, at 2520 rows, the
+    memory-only pattern in each row shape that covers a 3072 row."""
+    dim = 3072
+    out = {"dim": dim, "sizes": [], "shapes": []}
+    for rows in SWEEP_ROWS:
+        d = inputs.make("ptok", rows=rows, dim=dim)
+        nbytes = algorithmic_bytes("ptok", d)
+        prod = Producer("ptok_sweep", d, sets_for(nbytes, True), torch, alnp, F)
+        k = time_producer(prod, steps, warmup, use_graph, torch, stream, repeats=repeats)
+        f = time_producer(prod, steps, warmup, use_graph, torch, stream, floor=True, repeats=repeats)
+        cp = CopyCeiling(nbytes, True, torch, F)
+        c = time_launches(torch, stream, cp.launch, cp.sets, steps, warmup, use_graph, repeats)
+        row = {"rows": rows, "bytes": nbytes, "kernel_us": round(k["us"], 3),
+               "floor_us": round(f["us"], 3), "copy_us": round(c["us"], 3),
+               "kernel_frac_of_peak": round(nbytes / k["us"] / 1e3 / HBM_PEAK_GBS, 4),
+               "floor_frac_of_peak": round(nbytes / f["us"] / 1e3 / HBM_PEAK_GBS, 4),
+               "copy_frac_of_peak": round(cp.nbytes / c["us"] / 1e3 / HBM_PEAK_GBS, 4)}
+        out["sizes"].append(row)
+        print(f"# sweep {rows}x{dim}: kernel {row['kernel_us']} us, floor {row['floor_us']} us, "
+              f"copy {row['copy_us']} us", file=sys.stderr, flush=True)
+        if rows == 2520:
+            for waves, vpt in SWEEP_SHAPES:
+                def launch(i, h, prod=prod, waves=waves, vpt=vpt):
+                    fn, args = prod.floor_calls[i % prod.sets]
+                    st = F.alnp_floor_rows_shape(*args, waves, vpt, h)
+                    if st != 0:
+                        raise RuntimeError(f"floor shape {waves}x{vpt}: status {st}")
+                t = time_launches(torch, stream, launch, prod.sets, steps, warmup, use_graph,
+                                  repeats)
+                out["shapes"].append({"waves": waves, "vpt": vpt, "us": round(t["us"], 3),
+                                      "frac_of_peak": round(nbytes / t["us"] / 1e3 / HBM_PEAK_GBS, 4)})
+                print(f"# shape {waves}x{vpt}: {t['us']:.3f} us", file=sys.stderr, flush=True)
+        del prod, cp
+        torch.cuda.empty_cache()
+    b = np.array([r["bytes"] for r in out["sizes"]], np.float64)
+    for key in ("kernel_us", "floor_us", "copy_us"):
+        t = np.array([r[key] for r in out["sizes"]], np.float64)
+        slope, icpt = np.polyfit(b, t, 1)
+        out[key.replace("_us", "_fit")] = {"intercept_us": round(float(icpt), 3),
+                                           "slope_gbs": round(float(1e-3 / slope), 1)}
+    print(json.dumps({"floor_sweep": out, "steps": steps, "repeats": repeats}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the producers are "
                           "row-independent and would shard rows across GPUs with no "
                           "exchange, but no multi-GPU path is built", "n_gpus": a.gpus}))
+        sys.exit(2)
+    modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]
+    err = counter_guard(a, modes)
+    if err:
+        print(json.dumps({"error": err, "modes": modes, "steps": a.steps}))
         sys.exit(2)
     import torch
 
@@ -490,13 +883,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     use_graph = not a.direct
+    repeats = 1 if a.counters else max(1, a.repeats)
+    F = None if (a.no_floor or a.counters) else floor_lib()
     if a.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "copies": 4}))
+        calibrate_copy(torch, floor_lib())
+        return
+    stream = torch.cuda.Stream()
+    if a.floor_sweep:
+        if F is None:
+            print(json.dumps({"error": "--floor-sweep needs libalnp_floor.so"}))
+            sys.exit(2)
+        floor_sweep(torch, alnp, inputs, F, stream, a.steps, a.warmup, use_graph, repeats)
         return
 
     head = "ptok_fp8_2520x3072"
@@ -506,12 +903,9 @@ def main():
         "mxfp8_ptok_2520x3072", "mxfp8_table_2520x3072", "ln_mxfp4_4096x3072"]
     if a.only:
         names = [n for n in a.only.split(",") if n]
-    modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]
     results = {}
     head_inputs = None
-    stream = torch.cuda.Stream()
-    F = None if a.no_floor else floor_lib()
-    if F is None and not a.no_floor:
+    if F is None and not (a.no_floor or a.counters):
         print("# libalnp_floor.so not built: no practical floors", file=sys.stderr, flush=True)
     for name in names:
         if name == "ln_fp8_2520x3072":
@@ -529,30 +923,48 @@ def main():
         nbytes = algorithmic_bytes(name, d)
         r = {"bytes": nbytes}
         for mode in modes:
-            sets = sets_for(nbytes, mode == "cold")
-            prod = Producer(name, d, sets, torch, alnp, F if mode == "cold" else None)
-            us = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream)
-            r[mode] = {"us_per_call": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
-                       "sets": sets, "footprint_mb": round(sets * nbytes / 2**20, 1)}
+            cold = mode == "cold"
+            sets = sets_for(nbytes, cold)
+            print(f"# timing {name} {mode}: {sets} buffer sets, {a.steps} steps x {repeats}",
+                  file=sys.stderr, flush=True)
+            prod = Producer(name, d, sets, torch, alnp, F if cold else None)
+            t = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, repeats=repeats)
+            rec = rounded(t)
+            rec.update({"gbs": round(nbytes / t["us"] / 1e3, 1), "sets": sets,
+                        "footprint_mb": round(sets * nbytes / 2**20, 1)})
             if prod.floor_calls:
-                fus = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, floor=True)
-                r[mode]["floor_us"] = round(fus, 3)
-                r[mode]["floor_frac_of_peak"] = round(nbytes / fus / 1e3 / HBM_PEAK_GBS, 4)
-                r[mode]["frac_of_floor"] = round(fus / us, 4)
+                f = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, floor=True,
+                                  repeats=repeats)
+                rec["floor_us"] = round(f["us"], 3)
+                rec["floor_us_range"] = [round(f["min"], 3), round(f["max"], 3)]
+                rec["floor_frac_of_peak"] = round(nbytes / f["us"] / 1e3 / HBM_PEAK_GBS, 4)
+                rec["frac_of_floor"] = round(f["us"] / t["us"], 4)
             del prod
+            if cold and F is not None:
+                cp = CopyCeiling(nbytes, True, torch, F)
+                c = time_launches(torch, stream, cp.launch, cp.sets, a.steps, a.warmup, use_graph,
+                                  repeats)
+                rec["copy_us"] = round(c["us"], 3)
+                rec["copy_frac_of_peak"] = round(cp.nbytes / c["us"] / 1e3 / HBM_PEAK_GBS, 4)
+                del cp
+            r[mode] = rec
             torch.cuda.empty_cache()
-        floor_note = ""
+        note = ""
         if "cold" in r and "floor_us" in r["cold"]:
             c = r["cold"]
-            floor_note = (f"; memory-only floor {c['floor_us']} us "
-                          f"({100 * c['floor_frac_of_peak']:.1f}% of peak), "
-                          f"kernel at {100 * c['frac_of_floor']:.1f}% of it")
-        print(f"# {name}: " + ", ".join(f"{m} {r[m]['us_per_call']} us ({r[m]['gbs']} GB/s)"
-                                        for m in modes) + floor_note, file=sys.stderr, flush=True)
+            note = (f"; memory-only floor {c['floor_us']} us "
+                    f"({100 * c['floor_frac_of_peak']:.1f}% of peak), "
+                    f"kernel at {100 * c['frac_of_floor']:.1f}% of it")
+        if "cold" in r and "copy_us" in r["cold"]:
+            note += f"; copy of the same bytes {r['cold']['copy_us']} us"
+        print(f"# {name}: " + ", ".join(
+            f"{m} {r[m]['us_per_call']} us [{r[m]['us_min']}, {r[m]['us_max']}] "
+            f"({r[m]['gbs']} GB/s)" for m in modes) + note, file=sys.stderr, flush=True)
         results[name] = r
 
     if head not in results or "cold" not in results[head] or "warm" not in results[head]:
-        print(json.dumps({"partial": True, "rows": results}), flush=True)
+        print(json.dumps({"partial": True, "steps": a.steps, "repeats": repeats,
+                          "rows": results}), flush=True)
         return
     h = results[head]
     us = h["cold"]["us_per_call"]
@@ -574,10 +986,16 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.1) per-token scale/shift, bf16)",
         "config": {"workload": head, "rows": 2520, "dim": 3072, "act_scale": 0.025,
-                   "eps": 1e-5, "timing": "cold", "buffer_sets": h["cold"]["sets"],
+                   "eps": 1e-5, "io": "bf16 in, e4m3 out, fp32 arithmetic",
+                   "timing": "cold", "buffer_sets": h["cold"]["sets"],
                    "footprint_mb": h["cold"]["footprint_mb"],
-                   "launch": "hipgraph" if use_graph else "direct"},
+                   "launch": "hipgraph" if use_graph else "direct",
+                   "repeats": repeats,
+                   "statistic": f"median of {repeats} timed windows of exactly {a.steps} "
+                                "launches, each between two event-record nodes of one graph "
+                                "that first rotates through every buffer set untimed"},
         "us_per_call": us,
+        "us_range": [h["cold"]["us_min"], h["cold"]["us_max"]],
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "warm_us_per_call": h["warm"]["us_per_call"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -586,16 +1004,21 @@ def main():
                      "algorithmic_bytes_per_launch": h["bytes"]},
         "rows": {k: v for k, v in results.items() if k != head},
     }
-    if "floor_us" in h["cold"]:
-        c = h["cold"]
+    c = h["cold"]
+    if "floor_us" in c:
         line["roofline"]["practical_floor"] = {
             "us": c["floor_us"], "achieved": round(h["bytes"] / c["floor_us"] / 1e3, 1),
             "frac_of_peak": c["floor_frac_of_peak"], "kernel_frac_of_floor": c["frac_of_floor"],
             "what": "memory-only counterpart (libalnp_floor.so): the same loads and stores in "
                     "the producer's row shape, no arithmetic, timed the same way"}
-    if not a.no_overhead and not a.only_headline and not a.only:
-        line["launch_overhead"] = launch_overhead(torch, alnp, inputs, stream)
-    if not a.no_cpu_baseline:
+    if "copy_us" in c:
+        line["roofline"]["copy_ceiling"] = {
+            "us": c["copy_us"], "frac_of_peak": c["copy_frac_of_peak"],
+            "what": "plain device copy (alnp_floor_copy) of the same number of bytes, half read "
+                    "and half written, timed the same way"}
+    if not (a.no_overhead or a.only_headline or a.only or a.counters):
+        line["launch_overhead"] = launch_overhead(torch, alnp, inputs, stream, repeats=repeats)
+    if not (a.no_cpu_baseline or a.counters):
         line["cpu_baseline"] = cpu_baseline(head_inputs, h["bytes"])
     print(json.dumps(line), flush=True)
 

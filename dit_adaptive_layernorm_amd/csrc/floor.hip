@@ -158,6 +158,29 @@ __global__ __launch_bounds__(256) void k_floor_mod6(FloorMod6Args a)
     }
 }
 
+// Plain device-to-device copy, the practical ceiling for a stream of
+// a given size: each thread moves kCopyVecs 16-byte vectors, 256 threads
+// apart (every load instruction of a wave covers 1 KiB), with the same
+// non-temporal loads and stores as the producers.
+constexpr int kCopyVecs = 4;
+
+__global__ __launch_bounds__(256) void k_floor_copy(const uint4* src, uint4* dst, int64_t nvec)
+{
+    const int64_t base = (int64_t)blockIdx.x * (256 * kCopyVecs) + threadIdx.x;
+    uint4 v[kCopyVecs];
+#pragma unroll
+    for (int k = 0; k < kCopyVecs; ++k) {
+        const int64_t i = base + k * 256;
+        v[k] = i < nvec ? ld_stream(src + i) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyVecs; ++k) {
+        const int64_t i = base + k * 256;
+        if (i < nvec)
+            st_stream(dst + i, v[k]);
+    }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -175,9 +198,43 @@ using namespace alnp;
 // Returns 0, or -1 for a shape or pointer the row kernels do not take (dim
 // not a multiple of 32, rows longer than the register-resident row shapes,
 // unaligned pointers), -2 for an unknown out_kind, -6 for a launch failure.
+static int floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b, int64_t ab_stride,
+                      int64_t rows, int dim, int out_kind, void* out, uint8_t* scales,
+                      RowShape rs, hipStream_t stream);
+
 extern "C" int alnp_floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b,
                                int64_t ab_stride, int64_t rows, int dim, int out_kind, void* out,
                                uint8_t* scales, hipStream_t stream)
+{
+    return floor_rows(x, a, b, ab_stride, rows, dim, out_kind, out, scales,
+                      dim > 0 ? row_shape(dim) : RowShape{0, 0}, stream);
+}
+
+// The same memory-only row kernel in a row shape given by the caller (waves
+// per row: 1, 2, 4 or 8; 16-byte vectors per thread: 1..8), for comparing
+// access patterns at one size.  The shape must cover the row, with only each
+// thread's last vector slot allowed past its end: waves * 64 * vpt >= dim / 8
+// and (vpt - 1) * waves * 64 <= dim / 8.  Same arguments and returns as
+// alnp_floor_rows; -1 also for a shape that breaks these rules.
+extern "C" int alnp_floor_rows_shape(const uint16_t* x, const uint16_t* a, const uint16_t* b,
+                                     int64_t ab_stride, int64_t rows, int dim, int out_kind,
+                                     void* out, uint8_t* scales, int waves, int vpt,
+                                     hipStream_t stream)
+{
+    if (waves != 1 && waves != 2 && waves != 4 && waves != 8)
+        return -1;
+    if (vpt < 1 || vpt > 8 || dim <= 0 || dim % 32 != 0)
+        return -1;
+    const int nvec = dim / 8;
+    if (waves * 64 * vpt < nvec || (vpt - 1) * waves * 64 > nvec)
+        return -1;
+    return floor_rows(x, a, b, ab_stride, rows, dim, out_kind, out, scales,
+                      RowShape{waves * 64, vpt}, stream);
+}
+
+static int floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b, int64_t ab_stride,
+                      int64_t rows, int dim, int out_kind, void* out, uint8_t* scales,
+                      RowShape rs, hipStream_t stream)
 {
     if (rows <= 0)
         return 0;
@@ -188,7 +245,6 @@ extern "C" int alnp_floor_rows(const uint16_t* x, const uint16_t* a, const uint1
     const bool want_scales = out_kind == kOutNvfp4 || out_kind == kOutMxfp8 || out_kind == kOutMxfp4;
     if (want_scales && !scales)
         return -1;
-    const RowShape rs = row_shape(dim);
     if (rs.vpt == 0)
         return -1;
     FloorRowArgs f{x, a, b, ab_stride, rows, dim, static_cast<uint8_t*>(out), scales};
@@ -226,5 +282,23 @@ extern "C" int alnp_floor_modulation6(const float* params, int64_t tokens, int d
     const int64_t gy = groups < 65535 ? groups : 65535;
     const dim3 grid((unsigned)((slots + 255) / 256), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
     hipLaunchKernelGGL(k_floor_mod6, grid, dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Plain copy of nbytes from src to dst (device pointers, 16-byte aligned,
+// nbytes a multiple of 16 and at most 2^40).  Returns 0, -1 (shape,
+// pointer) or -6.
+extern "C" int alnp_floor_copy(const void* src, void* dst, int64_t nbytes, hipStream_t stream)
+{
+    if (nbytes == 0)
+        return 0;
+    if (!src || !dst || nbytes < 0 || nbytes % 16 != 0 || nbytes > (int64_t(1) << 40) ||
+        !aligned16(src) || !aligned16(dst))
+        return -1;
+    const int64_t nvec = nbytes / 16;
+    const int64_t per_block = 256 * kCopyVecs;
+    const dim3 grid((unsigned)((nvec + per_block - 1) / per_block));
+    hipLaunchKernelGGL(k_floor_copy, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), nvec);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }

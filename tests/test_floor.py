@@ -24,6 +24,11 @@ def floor_lib():
     F.alnp_floor_rows.restype = ctypes.c_int
     F.alnp_floor_modulation6.argtypes = [vp, i64, ctypes.c_int, ctypes.POINTER(vp), vp]
     F.alnp_floor_modulation6.restype = ctypes.c_int
+    F.alnp_floor_rows_shape.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                                        ctypes.c_int, ctypes.c_int, vp]
+    F.alnp_floor_rows_shape.restype = ctypes.c_int
+    F.alnp_floor_copy.argtypes = [vp, vp, i64, vp]
+    F.alnp_floor_copy.restype = ctypes.c_int
     return F
 
 
@@ -45,6 +50,20 @@ def test_floor_library_exports_and_rejects_bad_arguments():
     assert F.alnp_floor_modulation6(A, 4, 60, outs, None) == -1
     outs[3] = None
     assert F.alnp_floor_modulation6(A, 4, 64, outs, None) == -1
+    # Explicit row shapes: the shape must cover the row (dim 3072 = 384
+    # vectors), with only the last vector slot past its end.
+    shape = lambda w, v, dim=3072: F.alnp_floor_rows_shape(A, None, None, 0, 0, dim, FP8, B, None,
+                                                           w, v, None)
+    for w, v in ((1, 6), (2, 3), (4, 2), (8, 1)):
+        assert shape(w, v) == 0
+    for w, v in ((3, 2), (1, 5), (2, 2), (4, 3), (8, 2), (2, 0), (2, 9)):
+        assert shape(w, v) == -1, (w, v)
+    # Copies: 16-byte multiples of 16-byte aligned pointers.
+    assert F.alnp_floor_copy(A, B, 0, None) == 0
+    assert F.alnp_floor_copy(A, B, 24, None) == -1
+    assert F.alnp_floor_copy(A + 8, B, 32, None) == -1
+    assert F.alnp_floor_copy(None, B, 32, None) == -1
+    assert F.alnp_floor_copy(A, B, -16, None) == -1
 
 
 def xor_words(x, a=None, b=None):
@@ -142,3 +161,42 @@ def test_floor_modulation6_stores_the_six_outputs(tokens, dim):
     for k in range(6):
         want = (p[:, k, :] >> 16).astype(np.uint16)
         assert np.array_equal(outs[k].cpu().numpy().view(np.uint16), want), k
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("waves,vpt", [(1, 6), (2, 3), (4, 2), (8, 1)])
+def test_floor_rows_shape_stores_the_same_bytes(waves, vpt):
+    """Every row shape of the per-token pattern stores the same bytes."""
+    import torch
+    F = floor_lib()
+    rows, dim = 5, 3072
+    print(f"floor rows shape {waves}x{vpt} {rows}x{dim}", flush=True)
+    r = np.random.default_rng(waves * 10 + vpt)
+    u16 = lambda shape: r.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    dev = lambda h: torch.from_numpy(h.view(np.int16)).cuda()
+    x, a, b = u16((rows, dim)), u16((rows, dim)), u16((rows, dim))
+    want, _ = expected_rows(FP8, x, a, b)
+    out = torch.full((rows * dim,), 0xA5, dtype=torch.uint8, device="cuda")
+    xd, ad, bd = dev(x), dev(a), dev(b)
+    st = F.alnp_floor_rows_shape(xd.data_ptr(), ad.data_ptr(), bd.data_ptr(), dim, rows, dim, FP8,
+                                 out.data_ptr(), None, waves, vpt,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), np.ascontiguousarray(want).view(np.uint8).reshape(-1))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16, 16 * 1023, 16 * 1024 * 5 + 48, 27095040])
+def test_floor_copy_copies(nbytes):
+    import torch
+    F = floor_lib()
+    print(f"floor copy {nbytes} bytes", flush=True)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((nbytes + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    st = F.alnp_floor_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0x5A).all())
