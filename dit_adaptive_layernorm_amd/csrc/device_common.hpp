@@ -263,12 +263,24 @@ __device__ __forceinline__ void sat448x8(float (&v)[8])
         v[e] = sat448(v[e]);
 }
 
+// Max of two non-negative floats that are not NaN (block maxima from
+// absmax8): their bit patterns order as unsigned integers.  One integer max
+// takes the DPP operand directly, where fmaxf would also need a zero for the
+// DPP move's inactive value and a canonicalizing max.
+template <int CTRL>
+__device__ __forceinline__ float max_nonneg_dpp(float v)
+{
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t p = __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false);
+    return __uint_as_float(b > p ? b : p);
+}
+
 // Max over the four lanes of a quad (the lanes holding one 32-element MX
-// block): quad_perm [1,0,3,2] then [2,3,0,1].
+// block): quad_perm [1,0,3,2] then [2,3,0,1].  v >= 0, not NaN.
 __device__ __forceinline__ float quad_max(float v)
 {
-    v = fmaxf(v, dpp<0xB1>(v));
-    return fmaxf(v, dpp<0x4E>(v));
+    v = max_nonneg_dpp<0xB1>(v);
+    return max_nonneg_dpp<0x4E>(v);
 }
 
 // Exponent E of an MX block scale 2^E (OCP Microscaling Formats v1.0):
@@ -283,10 +295,18 @@ __device__ __forceinline__ int mx_scale_exp(float amax, int emax)
 }
 
 // Max of a lane and its xor-1 partner (the two lanes holding one 16-element
-// FP4 block).
+// FP4 block).  v >= 0, not NaN.
 __device__ __forceinline__ float pair_max(float v)
 {
-    return fmaxf(v, dpp<0xB1>(v));
+    return max_nonneg_dpp<0xB1>(v);
+}
+
+// e4m3 code of one float already in range (|v| <= 448), in the low byte:
+// one v_cvt_pk_fp8_f32 (the other converted value and the upper half of the
+// word are discarded).
+__device__ __forceinline__ uint32_t e4m3_code1(float v)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, __float_as_int(v), false) & 0xFFu;
 }
 
 }  // namespace alnp

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
             b[e + 1] = bf16_hi(w);
         }
         const float amax = pair_max(absmax8(b));
-        const uint32_t scode = pack_e4m3x4(fminf(amax * kSixth, 448.0f), 0.f, 0.f, 0.f) & 0xFFu;
+        const uint32_t scode = e4m3_code1(fminf(amax * kSixth, 448.0f));
         // A zero scale gives zero codes (a select, not a branch: inv_s[0] is
         // 0 and would leave the signs of negative values).
         const float enc = inv_s[scode];

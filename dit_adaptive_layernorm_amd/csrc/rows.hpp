@@ -9,10 +9,12 @@
 //    parameter, so launch bounds and indexing are compile-time), each thread
 //    holding VPT 16-byte vectors of the row (vector i = v * threads + t), so every load
 //    instruction of a wave covers 1 KiB of contiguous memory.  For dim 3072:
-//    two waves, three vectors per thread.  The row stays in registers: x,
-//    then the per-token operands, are requested up front so their latency
-//    overlaps; mean and variance are two passes over registers with DPP wave
-//    reductions and one LDS exchange between the waves.  Spreading a row over
+//    two waves, three vectors per thread.  The row stays in registers: x is
+//    requested up front, operands shared by every row with it, and streamed
+//    per-row operands once the row statistics are known (their bytes then
+//    arrive while the statistics run); mean and variance are two passes
+//    over registers with DPP wave reductions and one LDS exchange between
+//    the waves.  Spreading a row over
 //    several waves keeps the serial arithmetic each wave does after its data
 //    arrives short, which is what bounds the end of the kernel.  Streamed
 //    operands use non-temporal loads and the outputs non-temporal stores.
@@ -48,17 +50,24 @@ __device__ __forceinline__ uint4 ld_row(const uint16_t* row, int i, int nvec, bo
 // the mean.  mean = sum * (1/dim), var = sum_sq * (1/dim), rstd = 1/sqrt(var
 // + eps), all fp32.  The deviations x - mean are returned in d for the
 // caller's pass over the row.  `reduce` sums a value over the row's waves
-// and takes the slot index (0 or 1) of its LDS partials.
+// and takes the slot index (0 or 1) of its LDS partials.  row_mean and
+// row_rstd are the two passes on their own, for callers that issue loads
+// between them; row_stats runs both.
 template <int VPT, typename Reduce>
-__device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], bool tail_ok, float inv_dim,
-                                          float eps, Reduce reduce, float (&d)[VPT][8],
-                                          float& mean, float& rstd)
+__device__ __forceinline__ float row_mean(const uint4 (&xv)[VPT], float inv_dim, Reduce reduce)
 {
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         s = sum_bf16x8(xv[v], s);
-    mean = reduce(s, 0) * inv_dim;
+    return reduce(s, 0) * inv_dim;
+}
+
+template <int VPT, typename Reduce>
+__device__ __forceinline__ float row_rstd(const uint4 (&xv)[VPT], bool tail_ok, float mean,
+                                          float inv_dim, float eps, Reduce reduce,
+                                          float (&d)[VPT][8])
+{
     float q = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -74,7 +83,16 @@ __device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], bool tail_ok, 
         }
     }
     const float var = reduce(q, 1) * inv_dim;
-    rstd = rsqrt_refined(var + eps);
+    return rsqrt_refined(var + eps);
+}
+
+template <int VPT, typename Reduce>
+__device__ __forceinline__ void row_stats(const uint4 (&xv)[VPT], bool tail_ok, float inv_dim,
+                                          float eps, Reduce reduce, float (&d)[VPT][8],
+                                          float& mean, float& rstd)
+{
+    mean = row_mean<VPT>(xv, inv_dim, reduce);
+    rstd = row_rstd<VPT>(xv, tail_ok, mean, inv_dim, eps, reduce, d);
 }
 
 // Row index of a workgroup in the 2-D grid (x fastest); the grid can hold
