@@ -60,9 +60,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         for (int v = 0; v < VPT; ++v)
             xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, !FULL && v == VPT - 1);
 
-        // Modulation operands, requested before the reductions.  Per-token
-        // rows and temb chunks are streamed; (dim,) vectors are shared by
-        // every row and kept in cache.
+        // Modulation operands shared by every row ((dim,) vectors, kept in
+        // cache) are requested with x; streamed per-row operands
+        // (load_streamed below) after the row statistics.
         uint4 scv[NB], shv[NB];
         uint2 sc8[N8], sh8[N8];
         uint4 isv[NI];
