@@ -572,7 +572,9 @@ def time_launches(torch, stream, launch, sets, steps, warmup, use_graph, repeats
                 samples.append(E.elapsed_ms(a, b) * 1000.0 / steps)
                 E.free(a, b)
     us = sorted(samples)
-    return {"us": float(np.median(us)), "min": us[0], "max": us[-1]}
+    return {"us": float(np.median(us)), "min": us[0], "max": us[-1], "spacer": nspace,
+            "launches": warmup + 16 + (2 if use_graph else 1) * repeats *
+                        (nspace + steps + (TAIL_LAUNCHES if use_graph else 0))}
 
 
 def time_producer(prod, steps, warmup, use_graph, torch, stream, floor=False, repeats=REPEATS):
@@ -929,7 +931,12 @@ def main():
                   file=sys.stderr, flush=True)
             prod = Producer(name, d, sets, torch, alnp, F if cold else None)
             t = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, repeats=repeats)
+            print(f"# launches {name} {mode} producer: warmup {a.warmup}, burst 16, spacer "
+                  f"{t['spacer']}, steps {a.steps}, tail {TAIL_LAUNCHES if use_graph else 0}, "
+                  f"repeats {repeats}, graph {int(use_graph)}, total {t['launches']}",
+                  file=sys.stderr, flush=True)
             rec = rounded(t)
+            rec["spacer_launches"] = t["spacer"]
             rec.update({"gbs": round(nbytes / t["us"] / 1e3, 1), "sets": sets,
                         "footprint_mb": round(sets * nbytes / 2**20, 1)})
             if prod.floor_calls:
