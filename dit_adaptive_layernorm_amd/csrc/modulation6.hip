@@ -1,9 +1,9 @@
 // modulation6.hip -- six-way DiT modulation producer for gfx950.
 //
 // out_k[t, :] = bf16_rne(params[t, k, :] + mod[k, :]) for k = 0..5
-// ("adaptive-layernorm-producers" README, "Tensor Contract": FP32
-// (batch, sequence, 6, dim) parameters plus FP32 (6, dim) layer modulation,
-// six BF16 (batch, sequence, dim) outputs).
+// ("adaptive-layernorm-producers" README, "Tensor Contract": fp32 params of
+// shape (batch, seq, 6, dim) and an fp32 (6, dim) per-layer table in, six
+// bf16 (batch, seq, dim) tensors out).
 //
 // A pure stream: 4 bytes read and 2 written per element, one add.  Each
 // thread owns one 8-element slot of the (6, dim) span and handles it for four

@@ -99,8 +99,9 @@ int alnp_ada_layer_norm_quant_fp8_bf16(const uint16_t* x, const uint16_t* scale,
                                        void* stream);
 
 /*
- * Per-token AdaLN -> FP8 (README: ada_layer_norm_quant_fp8_ptok_bf16,
- * "per-token modulation without materializing a broadcast buffer").
+ * Per-token AdaLN -> FP8 (README "Available Functions":
+ * ada_layer_norm_quant_fp8_ptok_bf16; each activation row has its own
+ * scale/shift row, read directly instead of from a broadcast copy).
  *   scale, shift  (rows, dim) bf16, one row of operands per activation row.
  * Other arguments as for the broadcast form.
  */
@@ -113,9 +114,9 @@ int alnp_ada_layer_norm_quant_fp8_ptok_bf16(const uint16_t* x,
                                             float* row_rstd, void* stream);
 
 /*
- * Table-form per-token AdaLN -> FP8 (README:
- * ada_layer_norm_quant_fp8_ptok_table_bf16, "fused host modulation table add
- * and chunk selection").
+ * Table-form per-token AdaLN -> FP8 (README "Available Functions":
+ * ada_layer_norm_quant_fp8_ptok_table_bf16; the kernel picks the scale and
+ * shift chunks of temb itself and adds the fp32 table row to each).
  *   temb       (rows, chunks, dim) bf16
  *   table      (chunks, dim) fp32
  *   shift_idx, scale_idx  chunk indices in [0, chunks); they may be equal
@@ -197,7 +198,7 @@ int64_t alnp_sf_size(int64_t rows, int64_t dim);
 /*
  * LayerNorm (no affine) -> FP4 with the block scales in the 128x4 tiled
  * ("swizzled") layout (README: layer_norm_no_affine_quant_nvfp4_swizzled_bf16;
- * "Tensor Contract": "128x4 swizzled uint8 scale layout", allocate with
+ * "Tensor Contract": scale bytes in a 128x4 tiled layout, sized by
  * swizzled_sf_size).  The pages name the layout without defining it; this is
  * the tiled layout NVIDIA documents for block-scaled GEMM operands:
  *   cols = dim / 16 scales per row; tiles of 128 rows x 4 scales, 512 bytes
@@ -253,8 +254,8 @@ int64_t alnp_swizzled_sf_size(int64_t rows, int64_t dim);
 
 /*
  * Six-way DiT modulation (README: adaln_modulation6_bf16; "Tensor Contract":
- * FP32 (batch, sequence, 6, dim) parameters plus FP32 (6, dim) layer
- * modulation, six BF16 (batch, sequence, dim) outputs).
+ * fp32 params of shape (batch, seq, 6, dim) and an fp32 (6, dim) per-layer
+ * table in, six bf16 (batch, seq, dim) tensors out).
  *   params     (batch, seq, 6, dim) fp32
  *   layer_mod  (6, dim) fp32
  *   out        HOST array of 6 device pointers; out[k] is (batch, seq, dim)
@@ -357,9 +358,9 @@ int64_t alnp_mx_scale_size(int64_t rows, int64_t dim);
  * RMSNorm with segment-selected AdaLN modulation -> bf16.  Sources: the
  * RL-Kernel norm_modulate page (a modulated RMSNorm with an RMSNorm weight and
  * scale/shift rows picked per token by index_select) and the
- * h3-blackwell-runtime page ("Implementation Phases": RMSNorm output plus
- * segmented AdaLN scale/shift modulation; "NVFP4 Modulation Producer
- * Fusion", "Exactness Contract": segment-specific scale and shift, the
+ * h3-blackwell-runtime page ("Implementation Phases": an RMSNorm whose output
+ * is modulated with AdaLN scale/shift chosen per segment; "NVFP4 Modulation
+ * Producer Fusion", "Exactness Contract": per-segment operands, the
  * (x * (scale + 1)) + shift order, BF16 rounding).  Per row r, s = seg[r]:
  *   rstd = 1 / sqrt(sum_j x[r, j]^2 / dim + eps)     (fp32; no centring)
  *   n    = bf16_rne((x * rstd) * weight[j])          (weight 1 if NULL)
