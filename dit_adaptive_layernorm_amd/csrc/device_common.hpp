@@ -71,6 +71,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// bf16_rne(v) held as a float: one v_cvt_pk_bf16_f32 with a zero low half
+// leaves the bf16 pattern in the upper half and zeros below, which is the
+// float value of the bf16 (one instruction, where converting a pair and
+// unpacking it takes one and a half per element).
+__device__ __forceinline__ float bf16_round(float v)
+{
+    return __uint_as_float(pack_bf16x2(0.f, v));
+}
+
 // ---- e4m3 ----------------------------------------------------------------
 
 // Clamp to the e4m3 range, keeping NaN: IEEE 754-2019 minimum and maximum

@@ -172,13 +172,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
             a.sf[row * (dim >> 5) + (i >> 2)] = (uint8_t)(E + 127);
             continue;
         }
-        // Stage through bf16 (round to nearest even): one v_cvt_pk_bf16_f32
-        // per element with a zero low half leaves bf16(y) as the float's
-        // own bit pattern, where a packed pair would need unpacking (1
-        // instruction per element instead of 1.5).
+        // Stage through bf16 (round to nearest even), one convert per element.
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            b[e] = __uint_as_float(pack_bf16x2(0.f, y[e]));
+            b[e] = bf16_round(y[e]);
         const float amax = pair_max(absmax8(b));
         const uint32_t scode = e4m3_code1(fminf(amax * kSixth, 448.0f));
         // A zero scale gives zero codes (a select, not a branch: inv_s[0] is

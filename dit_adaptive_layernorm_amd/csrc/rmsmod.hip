@@ -8,23 +8,24 @@
 
 namespace alnp {
 
-// One modulated pair: the bf16 RMSNorm outputs n of two elements (already
-// rounded, packed), their operands, and the bf16 results packed.  Each step
-// is an fp32 operation rounded to bf16: t = bf16(scale + 1), u = bf16(n * t),
-// y = bf16(u + shift).  The second form takes t already computed (bf16
-// values held exactly in fp32).
-__device__ __forceinline__ uint32_t modulate_t_bf16x2(uint32_t n, float t0, float t1, float sh0,
-                                                      float sh1)
+// One modulated pair: the RMSNorm values of two elements before their bf16
+// rounding, their operands, and the bf16 results packed.  Each step is an
+// fp32 operation rounded to bf16: n = bf16(n), t = bf16(scale + 1),
+// u = bf16(n * t), y = bf16(u + shift).  The intermediate roundings keep
+// each value as a float (bf16_round); only y is packed.  The first form
+// takes t already computed (bf16 values held exactly in fp32).
+__device__ __forceinline__ uint32_t modulate_t_bf16x2(float n0, float n1, float t0, float t1,
+                                                      float sh0, float sh1)
 {
-    const uint32_t u = pack_bf16x2(bf16_lo(n) * t0, bf16_hi(n) * t1);
-    return pack_bf16x2(bf16_lo(u) + sh0, bf16_hi(u) + sh1);
+    const float u0 = bf16_round(bf16_round(n0) * t0);
+    const float u1 = bf16_round(bf16_round(n1) * t1);
+    return pack_bf16x2(u0 + sh0, u1 + sh1);
 }
 
-__device__ __forceinline__ uint32_t modulate_bf16x2(uint32_t n, float sc0, float sc1, float sh0,
-                                                    float sh1)
+__device__ __forceinline__ uint32_t modulate_bf16x2(float n0, float n1, float sc0, float sc1,
+                                                    float sh0, float sh1)
 {
-    const uint32_t t = pack_bf16x2(sc0 + 1.0f, sc1 + 1.0f);
-    return modulate_t_bf16x2(n, bf16_lo(t), bf16_hi(t), sh0, sh1);
+    return modulate_t_bf16x2(n0, n1, bf16_round(sc0 + 1.0f), bf16_round(sc1 + 1.0f), sh0, sh1);
 }
 
 // One workgroup per row, the row in registers (same shapes as the FP8
@@ -85,8 +86,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_rows(RmsArgs a)
                 n0 = n0 * w8[2 * k];
                 n1 = n1 * w8[2 * k + 1];
             }
-            o[k] = modulate_bf16x2(pack_bf16x2(n0, n1), sc[2 * k], sc[2 * k + 1], sh[2 * k],
-                                   sh[2 * k + 1]);
+            o[k] = modulate_bf16x2(n0, n1, sc[2 * k], sc[2 * k + 1], sh[2 * k], sh[2 * k + 1]);
             o[k] = in_range ? o[k] : 0x7FC07FC0u;
         }
         st_stream(a.out + row * dim + (int64_t)i * 8, make_uint4(o[0], o[1], o[2], o[3]));
@@ -156,11 +156,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
                 float sc[8];
                 unpack8(scv[v], sc);
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t tt = pack_bf16x2(sc[e] + 1.0f, sc[e + 1] + 1.0f);
-                    tv[v][e] = bf16_lo(tt);
-                    tv[v][e + 1] = bf16_hi(tt);
-                }
+                for (int e = 0; e < 8; ++e)
+                    tv[v][e] = bf16_round(sc[e] + 1.0f);
             }
             cur = srow;
         }
@@ -193,8 +190,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
                     n0 = n0 * w8[2 * e];
                     n1 = n1 * w8[2 * e + 1];
                 }
-                o[e] = modulate_t_bf16x2(pack_bf16x2(n0, n1), tv[v][2 * e], tv[v][2 * e + 1],
-                                         sh[2 * e], sh[2 * e + 1]);
+                o[e] = modulate_t_bf16x2(n0, n1, tv[v][2 * e], tv[v][2 * e + 1], sh[2 * e],
+                                         sh[2 * e + 1]);
                 o[e] = in_range ? o[e] : 0x7FC07FC0u;
             }
             st_stream(a.out + row * dim + (int64_t)i * 8, make_uint4(o[0], o[1], o[2], o[3]));
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(256) void k_rms_mod_block(RmsArgs a)
         float n = ldbf(xr, j) * rstd;
         if (a.weight)
             n = n * ldbf(a.weight, j);
-        const uint32_t y = modulate_bf16x2(pack_bf16x2(n, 0.f), ldbf(a.scale, srow * dim + j), 0.f,
+        const uint32_t y = modulate_bf16x2(n, 0.f, ldbf(a.scale, srow * dim + j), 0.f,
                                            ldbf(a.shift, srow * dim + j), 0.f);
         a.out[row * dim + j] = in_range ? (uint16_t)(y & 0xFFFFu) : (uint16_t)0x7FC0;
     }

@@ -161,3 +161,54 @@ def test_standalone_quantizer_at_its_limit(orc):
     torch.cuda.empty_cache()
     ref = orc.e4m3_encode_sat(vs * np.float32(1.0 / np.float32(0.025)))
     assert np.array_equal(got, ref)
+
+
+def test_empty_calls_leave_outputs_untouched():
+    """rows = 0 (tokens = 0, n = 0) is a no-op through the C ABI: status 0,
+    and output buffers sized for one row keep their sentinel bytes."""
+    import ctypes
+    L = alnp.lib()
+    dim = 3072
+    print("empty calls through the C ABI", flush=True)
+    dev = lambda n, dt: torch.zeros(n, dtype=dt, device="cuda")
+    x = dev(dim, torch.bfloat16)
+    sc = dev(dim, torch.bfloat16)
+    sh = dev(dim, torch.bfloat16)
+    temb = dev(6 * dim, torch.bfloat16)
+    table = dev(6 * dim, torch.float32)
+    act = torch.tensor([0.025], dtype=torch.float32, device="cuda")
+    seg = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sentinel = lambda n: torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    out8, packed, sf, mxs = sentinel(dim), sentinel(dim // 2), sentinel(512), sentinel(dim // 32)
+    out16 = sentinel(2 * dim)
+    stats = sentinel(8)
+    m6 = [sentinel(2 * dim) for _ in range(6)]
+    arr = (ctypes.c_void_p * 6)(*[o.data_ptr() for o in m6])
+    p = lambda t: t.data_ptr()
+    h = torch.cuda.current_stream().cuda_stream
+    calls = [
+        L.alnp_ada_layer_norm_quant_fp8_bf16(p(x), p(sc), p(sh), p(act), 1e-5, 0, dim, p(out8),
+                                             p(stats), p(stats), h),
+        L.alnp_ada_layer_norm_quant_fp8_ptok_bf16(p(x), p(sc), p(sh), p(act), 1e-5, 0, dim,
+                                                  p(out8), p(stats), p(stats), h),
+        L.alnp_ada_layer_norm_quant_fp8_ptok_table_bf16(p(x), p(temb), p(table), 6, 0, 1, p(act),
+                                                        1e-5, 0, dim, p(out8), p(stats),
+                                                        p(stats), h),
+        L.alnp_layer_norm_no_affine_quant_fp8_static_bf16(p(x), p(act), 1e-5, 0, dim, p(out8),
+                                                          p(stats), p(stats), h),
+        L.alnp_layer_norm_no_affine_quant_nvfp4_bf16(p(x), 1e-5, 0, dim, p(packed), p(sf),
+                                                     p(stats), p(stats), h),
+        L.alnp_layer_norm_no_affine_quant_mxfp8_bf16(p(x), 1e-5, 0, dim, p(out8), p(mxs),
+                                                     p(stats), p(stats), h),
+        L.alnp_layer_norm_no_affine_quant_mxfp4_bf16(p(x), 1e-5, 0, dim, p(packed), p(mxs),
+                                                     p(stats), p(stats), h),
+        L.alnp_adaln_modulation6_bf16(p(table), p(table), 1, 0, dim, arr, h),
+        L.alnp_gated_residual_bf16(p(x), p(x), p(x), 0, dim, 1, p(out16), h),
+        L.alnp_rms_norm_modulate_seg_bf16(p(x), p(x), p(sc), p(sh), p(seg), 1, 1e-5, 0, dim,
+                                          p(out16), p(stats), h),
+        L.alnp_quant_fp8_static_f32(p(table), p(act), 0, p(out8), h),
+    ]
+    torch.cuda.synchronize()
+    assert calls == [0] * len(calls), calls
+    for buf in (out8, packed, sf, mxs, out16, stats, *m6):
+        assert bool((buf == 0xA5).all())
