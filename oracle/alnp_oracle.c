@@ -41,7 +41,8 @@
  *      stage and block quantization (the pages fix the staging only for the
  *      LN entry; the plainest reading applies it to the modulated value).
  *  R12 Swizzled scales: NVIDIA's documented 128x4 tiled layout for block
- *      scale factors.  Parity unpinned: the pages give only its name.
+ *      scale factors (the pages give only its name).  Pinned against
+ *      PyTorch's own implementation of that documented layout.
  *  R13 Residual gate (h3 page, the residual-gate epilogue's numerical
  *      program: bf16 GEMM output, gate multiplication with its bf16
  *      boundary, bf16 residual added, final bf16 rounding):
@@ -580,7 +581,7 @@ void orc_adaln_fp4_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
 }
 
 /* ------------------------------------------------------------------------ */
-/* 128x4 tiled block-scale layout (R12; parity unpinned).                     */
+/* 128x4 tiled block-scale layout (R12).                                       */
 /* The (rows, cols) scale matrix is cut into tiles of 128 rows x 4 columns,   */
 /* stored one after another (tile row-major: all column tiles of the first    */
 /* 128 rows, then the next 128 rows), 512 bytes each.  Inside a tile the      */

@@ -3,7 +3,10 @@
 Functions" and "Tensor Contract": e4m3 (dim,) modulation with fp32
 dequantization scalars, per-channel bf16 inv_s, the AdaLN NVFP4 entry and
 its swizzled scale buffer sized by swizzled_sf_size)."""
+import os
+
 import numpy as np
+import pytest
 import torch
 
 from dit_adaptive_layernorm_amd import inputs
@@ -166,7 +169,48 @@ def test_adaln_fp4_modfp8_staging_is_bf16_of_fp8_modfp8_y(orc):
     assert np.array_equal(b, torch.from_numpy(y).to(torch.bfloat16).float().numpy())
 
 
-# ---- swizzled scale layout (parity unpinned: properties only) ---------------------
+# ---- swizzled scale layout ---------------------------------------------------------
+#
+# The pages name the layout (README "Tensor Contract": the 128x4 swizzled
+# uint8 scale layout of CUTLASS block-scaled GEMMs) but print no example.  The
+# layout is NVIDIA's documented block-scaling-factor layout; PyTorch ships its
+# own implementation of it for its scaled-matmul tests
+# (torch.testing._internal.common_quantized.to_blocked, written from the
+# cuBLAS documentation).  The first test compares the oracle with that library
+# routine, padding included; the property tests below stay as well.
+
+def _torch_to_blocked():
+    """torch's to_blocked, as installed.  Its module imports test-only
+    packages that are not installed here, so the two functions it needs
+    (ceil_div, to_blocked) are taken from the installed source file and run
+    unchanged."""
+    import ast
+    import importlib.util
+    spec = importlib.util.find_spec("torch.testing._internal")
+    if spec is None or not spec.submodule_search_locations:
+        pytest.skip("torch's testing helpers are not installed")
+    path = os.path.join(list(spec.submodule_search_locations)[0], "common_quantized.py")
+    if not os.path.exists(path):
+        pytest.skip("torch's block-scale layout helper is not installed")
+    tree = ast.parse(open(path).read(), path)
+    defs = [n for n in tree.body if isinstance(n, ast.FunctionDef) and n.name in ("ceil_div", "to_blocked")]
+    if len(defs) != 2:
+        pytest.skip("torch's block-scale layout helper has moved")
+    ns = {"torch": torch}
+    exec(compile(ast.Module(body=defs, type_ignores=[]), path, "exec"), ns)
+    return ns["to_blocked"]
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 4), (1, 1), (129, 5), (300, 48), (256, 192),
+                                       (4096, 192), (77, 96), (5, 3)])
+def test_swizzle_matches_torch_block_scale_layout(orc, rows, cols):
+    to_blocked = _torch_to_blocked()
+    rng = np.random.default_rng(rows * 1009 + cols)
+    sf = rng.integers(1, 256, size=(rows, cols), dtype=np.uint8)
+    ref = to_blocked(torch.from_numpy(sf)).numpy()
+    got = orc.sf_swizzle(sf)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
 
 def test_swizzle_is_a_bijection_onto_the_padded_buffer(orc):
     for rows, cols in ((128, 4), (256, 192), (300, 48), (1, 1), (4096, 192), (129, 5)):
