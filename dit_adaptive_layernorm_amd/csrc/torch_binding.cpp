@@ -3,12 +3,11 @@
 // Every function takes torch tensors, runs on the device of its first tensor
 // (as torch's own operators do), checks them (GPU, that device, dtype, shape,
 // contiguity), allocates the outputs it is not given, and calls the C ABI of
-// libalnp.so (include/alnp.h) on torch's current stream of that device: the
-// same steps as the ctypes functions in __init__.py, without the
-// Python-level checks and ctypes marshalling that cost about 3 us per call.
-// Nothing here computes; errors raise the same Python exception types as
-// those functions (ValueError, TypeError, and the package's AlnpError for a
-// status from the library).
+// libalnp.so (include/alnp.h) on torch's current stream of that device.
+// Doing this in C++ saves the Python-level checks and ctypes marshalling,
+// about 3 us per call.  Nothing here computes; errors raise ValueError,
+// TypeError, or the package's AlnpError for a status from the library.  The
+// tests check every function against an independent ctypes marshalling.
 #include <torch/extension.h>
 #include <c10/core/DeviceGuard.h>
 #include <c10/hip/HIPFunctions.h>
@@ -88,8 +87,8 @@ void on_call_device(const Tensor& t, const char* name)
                               t.device().str());
 }
 
-// GPU, device, dtype, (shape,) contiguity, in that order, as the ctypes
-// functions.
+// GPU, device, dtype, (shape,) contiguity, in that order (the order of the
+// first failing check decides the error).
 void dev(const Tensor& t, const char* name, at::ScalarType dt)
 {
     on_call_device(t, name);

@@ -1,5 +1,5 @@
-"""The compiled binding against the ctypes functions on the GPU: for every
-function, the same inputs give the same bytes (outputs, block scales, row
+"""The compiled binding against the independent ctypes marshalling of
+tests/ctypes_ref.py on the GPU: for every function, the same inputs give the same bytes (outputs, block scales, row
 statistics), with outputs allocated by the call or passed in; misuse raises
 the same exception type on both paths (dtype: TypeError; shape, contiguity:
 ValueError; a status from the library: AlnpError with the same status)."""
@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import ctypes_ref
 import dit_adaptive_layernorm_amd as alnp
 from dit_adaptive_layernorm_amd import inputs
 from parity import act, dev_bf16, dev_f32
@@ -71,7 +72,7 @@ def cases():
 
 
 # Functions that also fill row statistics (row_mean and / or row_rstd).
-STATS = {n: ("row_mean", "row_rstd") for n in alnp._COMPILED_NAMES
+STATS = {n: ("row_mean", "row_rstd") for n in alnp.NAMES
          if n not in ("quant_fp8_static_f32", "adaln_modulation6_bf16", "gated_residual_bf16",
                       "rms_norm_modulate_seg_bf16")}
 STATS["rms_norm_modulate_seg_bf16"] = ("row_rstd",)
@@ -90,13 +91,13 @@ def run(fn, args, stats):
     return as_bytes(r), {k: v.cpu().numpy().view(np.uint32) for k, v in kw.items()}
 
 
-@pytest.mark.parametrize("name", alnp._COMPILED_NAMES)
+@pytest.mark.parametrize("name", alnp.NAMES)
 def test_same_bytes_as_ctypes(name):
     print(f"binding {name}", flush=True)
     args = cases()[name]
     stats = STATS.get(name, ())
     got, got_s = run(getattr(alnp, name), args, stats)
-    ref, ref_s = run(getattr(alnp.ctypes_api, name), args, stats)
+    ref, ref_s = run(getattr(ctypes_ref, name), args, stats)
     got = got if isinstance(got, list) else [got]
     ref = ref if isinstance(ref, list) else [ref]
     assert len(got) == len(ref), name
@@ -122,14 +123,14 @@ def test_outputs_passed_in_are_written_and_returned():
     r6 = alnp.adaln_modulation6_bf16(params, mod, out=outs)
     assert [t.data_ptr() for t in r6] == [t.data_ptr() for t in outs]
     torch.cuda.synchronize()
-    ref = alnp.ctypes_api.adaln_modulation6_bf16(params, mod)
+    ref = ctypes_ref.adaln_modulation6_bf16(params, mod)
     for t, u in zip(r6, ref):
         assert torch.equal(t.view(torch.int16), u.view(torch.int16))
 
 
 def _errors(name, args, kwargs=None):
     out = []
-    for fn in (getattr(alnp, name), getattr(alnp.ctypes_api, name)):
+    for fn in (getattr(alnp, name), getattr(ctypes_ref, name)):
         with pytest.raises(Exception) as e:
             fn(*args, **(kwargs or {}))
         out.append(e.value)
@@ -166,9 +167,9 @@ def test_tensor_off_the_call_device_is_rejected(monkeypatch):
     args = cases()
     res, gate, proj = args["gated_residual_bf16"]
     before = res.clone()
-    monkeypatch.setattr(alnp, "_device_index", lambda: 1)
+    monkeypatch.setattr(ctypes_ref, "_device_index", lambda: 1)
     with pytest.raises(ValueError, match=r"must be on cuda:1, the device of the call, got cuda:0"):
-        alnp.ctypes_api.gated_residual_bf16(res, gate, proj, out=res)
+        ctypes_ref.gated_residual_bf16(res, gate, proj, out=res)
     monkeypatch.undo()
     torch.cuda.synchronize()
     assert torch.equal(res, before)
