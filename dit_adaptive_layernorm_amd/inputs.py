@@ -8,6 +8,8 @@ Recipe: numpy PCG64 seeded with SeedSequence([seed, stream_id]), one stream id
 per tensor; standard normal draws in float64, scaled by sigma, rounded to
 float32; bf16 tensors are then rounded to bf16 by torch's CPU conversion
 (round to nearest even).  bf16 tensors are returned as uint16 bit patterns.
+Tensors too large to draw on the host (calls past 2^32 elements) are drawn on
+the GPU instead (device_normal).
 
 The workloads follow the shapes the pages measure (Wan-video 2520 x 3072 and
 4096 x 3072 rows, the decode-action 16 x 2048 row block, the six-way
@@ -57,6 +59,24 @@ def outlier_bf16(shape, seed: int, stream: int, outlier_stream: int,
     mask = rng(seed, outlier_stream).random(shape) < p
     f = np.where(mask, f * np.float32(factor), f).astype(np.float32)
     return to_bf16_bits(f)
+
+
+# ---- device-side draws, for calls too large to draw on the host -------------
+
+def device_normal(shape, sigma: float, seed: int, stream: int, dtype=torch.bfloat16,
+                  device: str = "cuda", chunk: int = 1 << 28) -> torch.Tensor:
+    """N(0, sigma) drawn on the GPU: torch's generator for `device`, seeded
+    with (seed << 8) + stream, float32 draws of `chunk` elements at a time,
+    scaled by sigma and rounded to `dtype` by torch (round to nearest even).
+    Deterministic for a given seed, stream, shape and chunk.  Callers copy
+    the rows they check to the host."""
+    g = torch.Generator(device=device).manual_seed((seed << 8) + stream)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for a in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - a)
+        flat[a:a + n] = (torch.randn(n, generator=g, device=device) * sigma).to(dtype)
+    return out
 
 
 # ---- the five workloads ----------------------------------------------------
