@@ -868,9 +868,9 @@ def floor_sweep(torch, alnp, inputs, F, stream, steps, warmup, use_graph, repeat
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the producers are "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; the producers are "
                           "row-independent and would shard rows across GPUs with no "
-                          "exchange, but no multi-GPU path is built", "n_gpus": a.gpus}))
+                          "exchange, but no multi-GPU path exists", "n_gpus": a.gpus}))
         sys.exit(2)
     modes = [m for m in a.modes.split(",") if m in ("cold", "warm")]
     err = counter_guard(a, modes)
