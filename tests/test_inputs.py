@@ -42,3 +42,25 @@ def test_outlier_fraction():
     frac = np.mean(x != base)
     assert 0.008 < frac < 0.012
     assert np.abs(x).max() > 40
+
+
+def test_device_draws_deterministic_and_whole():
+    """The device-side generator (used for calls past 2^32 elements), run on
+    torch's CPU generator: the same seed and stream give the same tensor,
+    another stream another one; a size that is not a multiple of the chunk
+    is filled completely; spreads and dtypes as asked."""
+    import torch
+    kw = dict(device="cpu", chunk=1000)
+    a = inputs.device_normal((37, 129), 0.5, 3, inputs.STREAM["x"], **kw)
+    b = inputs.device_normal((37, 129), 0.5, 3, inputs.STREAM["x"], **kw)
+    c = inputs.device_normal((37, 129), 0.5, 3, inputs.STREAM["scale"], **kw)
+    assert a.dtype == torch.bfloat16 and a.shape == (37, 129)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    f = a.float()
+    assert abs(f.std().item() - 0.5) < 0.03
+    # The tail past the last whole chunk (37 * 129 = 4773 = 4 * 1000 + 773)
+    # is drawn too: no zeros left from the allocation.
+    assert torch.count_nonzero(f.view(-1)[4000:]).item() >= 770
+    p = inputs.device_normal((2, 3, 6, 8), 1.0, 3, inputs.STREAM["params"], dtype=torch.float32, **kw)
+    assert p.dtype == torch.float32 and p.shape == (2, 3, 6, 8)
