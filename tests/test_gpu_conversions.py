@@ -48,6 +48,24 @@ def test_fp8_convert_with_act_scale(orc):
     assert_e4m3_equal(v, got, orc.e4m3_encode_sat(v * np.float32(1.0 / np.float32(0.025))))
 
 
+@pytest.mark.parametrize("a", [0.3, 0.7, 1.0 / 3.0, 3.0, 1e-3, 123.4, 6.1e-5])
+def test_fp8_convert_with_inexact_reciprocal(orc, a):
+    """act_scale values whose reciprocal is not exact in fp32: the kernels take
+    1/act_scale as one correctly rounded fp32 division, as the oracle does, so
+    v * (1/act) and its code agree bit for bit.  Points just around every e4m3
+    midpoint (scaled back by the reciprocal) are the ones a reciprocal one ulp
+    off would move across a rounding boundary."""
+    print(f"fp8 convert act_scale={a}", flush=True)
+    af = np.float32(a)
+    inv = np.float32(1.0) / af
+    mids = e4m3_points()
+    rng = np.random.default_rng(int(af.view(np.uint32)))
+    rand = (rng.standard_normal(1 << 18) * 120.0).astype(np.float32)
+    v = np.concatenate([mids / inv, rand / inv]).astype(np.float32)
+    got = host_u8(alnp.quant_fp8_static_f32(dev_f32(v), act(float(af))))
+    assert_e4m3_equal(v, got, orc.e4m3_encode_sat((v * inv).astype(np.float32)))
+
+
 def test_bf16_convert_matches_oracle(orc):
     hi = np.arange(65536, dtype=np.uint32) << 16
     lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
