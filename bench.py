@@ -502,86 +502,106 @@ def spacer_length(sets, steps, launch_us=None):
 def time_launches(torch, stream, launch, sets, steps, warmup, use_graph, repeats=REPEATS):
     """Median, min and max microseconds per launch over `repeats` timed
     windows of exactly `steps` launches each (launch i uses buffer set
-    i mod sets), measured with HIP events on `stream`, the stream the
-    launches run on (HipEvents: no system-scope fence).
+    i mod sets): time_interleaved with one variant."""
+    return time_interleaved(torch, stream, [(launch, sets)], steps, warmup, use_graph, repeats)[0]
+
+
+def time_interleaved(torch, stream, variants, steps, warmup, use_graph, repeats=REPEATS):
+    """For each (launch, sets) in `variants`: median, min and max
+    microseconds per launch over `repeats` timed windows of exactly `steps`
+    launches each (launch i uses buffer set i mod sets), measured with HIP
+    events on `stream`, the stream the launches run on (HipEvents: no
+    system-scope fence).
 
     Each window is preceded by an untimed spacer of whole rotations over
-    the sets and at least SPACER_MS of work (spacer_length): every set the
-    window touches has been evicted by the rotation through all the others,
-    and the GPU has been under steady load for a while when the window
-    opens.
+    its variant's sets and at least SPACER_MS of work (spacer_length):
+    every set the window touches has been evicted by the rotation through
+    all the others, and the GPU has been under steady load for a while when
+    the window opens.
 
-    With a graph (the default), each repeat is one executable graph: the
+    With a graph (the default), each window is one executable graph: the
     spacer, an event-record node, the `steps` timed launches, a second
     event-record node and a short tail.  The cost of starting a graph
     launch (several microseconds on this runtime, paid once per launch
     however many kernels the graph holds) then falls before the spacer,
-    outside the window, which holds exactly the timed launches.  The
-    repeats' graphs are launched back to back, between two device
-    synchronizations, so the GPU does not idle between windows.  Without a
+    outside the window, which holds exactly the timed launches.  All
+    windows are launched back to back, between two device synchronizations,
+    so the GPU does not idle between them, and the variants alternate
+    window by window, in reverse order on odd repeats (A B C, C B A, ...):
+    a slow drift of the clock or the memory system then moves every
+    variant alike, and ratios between them (a producer against its
+    memory-only floor) do not depend on which was timed first.  Without a
     graph the launches are enqueued directly, the events recorded on the
-    stream."""
+    stream, in the same order."""
     E = hip_events()
     h = stream.cuda_stream
-    samples = []
+    nv = len(variants)
+    samples = [[] for _ in range(nv)]
+    spacers = []
+    order = [v for r in range(repeats) for v in (range(nv) if r % 2 == 0 else range(nv - 1, -1, -1))]
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            launch(i, h)
-        torch.cuda.synchronize()
-        # Rough per-launch time from a short untimed burst, to size the spacer.
-        a, b = E.new(), E.new()
-        E.record(a, stream)
-        for i in range(16):
-            launch(i, h)
-        E.record(b, stream)
-        torch.cuda.synchronize()
-        nspace = spacer_length(sets, steps, E.elapsed_ms(a, b) * 1000.0 / 16)
-        E.free(a, b)
+        for launch, sets in variants:
+            for i in range(warmup):
+                launch(i, h)
+            torch.cuda.synchronize()
+            # Rough per-launch time from a short untimed burst, to size the spacer.
+            a, b = E.new(), E.new()
+            E.record(a, stream)
+            for i in range(16):
+                launch(i, h)
+            E.record(b, stream)
+            torch.cuda.synchronize()
+            spacers.append(spacer_length(sets, steps, E.elapsed_ms(a, b) * 1000.0 / 16))
+            E.free(a, b)
         if use_graph:
             cap = torch.cuda.Stream()
-            parts = [E.capture(cap, launch, r) for r in
-                     (range(nspace), range(steps), range(steps, steps + TAIL_LAUNCHES))]
-            windows = []
-            for _ in range(repeats):
-                t0, t1 = E.new(), E.new()
-                windows.append((E.window_graph(*parts, t0, t1), t0, t1))
-            E.free_captured(*parts)
-            for ex, _, _ in windows:            # upload, untimed
-                E.launch_graph(ex, stream)
+            windows = []                          # per variant: [(exec, t0, t1)] * repeats
+            for (launch, _), nspace in zip(variants, spacers):
+                parts = [E.capture(cap, launch, r) for r in
+                         (range(nspace), range(steps), range(steps, steps + TAIL_LAUNCHES))]
+                ws = []
+                for _ in range(repeats):
+                    t0, t1 = E.new(), E.new()
+                    ws.append((E.window_graph(*parts, t0, t1), t0, t1))
+                E.free_captured(*parts)
+                windows.append(ws)
+            for ws in windows:                    # upload, untimed
+                for ex, _, _ in ws:
+                    E.launch_graph(ex, stream)
             torch.cuda.synchronize()
-            for ex, _, _ in windows:            # back to back: the GPU never idles
-                E.launch_graph(ex, stream)
+            nth = [0] * nv
+            for v in order:                       # back to back: the GPU never idles
+                E.launch_graph(windows[v][nth[v]][0], stream)
+                nth[v] += 1
             torch.cuda.synchronize()
-            for ex, t0, t1 in windows:
-                samples.append(E.elapsed_ms(t0, t1) * 1000.0 / steps)
-                E.free_graph(ex)
-                E.free(t0, t1)
+            for v, ws in enumerate(windows):
+                for ex, t0, t1 in ws:
+                    samples[v].append(E.elapsed_ms(t0, t1) * 1000.0 / steps)
+                    E.free_graph(ex)
+                    E.free(t0, t1)
         else:
             events = []
-            for _ in range(repeats):
+            for v in order:
+                launch, _ = variants[v]
                 t0, t1 = E.new(), E.new()
-                for i in range(nspace):
+                for i in range(spacers[v]):
                     launch(i, h)
                 E.record(t0, stream)
                 for i in range(steps):
                     launch(i, h)
                 E.record(t1, stream)
-                events.append((t0, t1))
+                events.append((v, t0, t1))
             torch.cuda.synchronize()
-            for a, b in events:
-                samples.append(E.elapsed_ms(a, b) * 1000.0 / steps)
+            for v, a, b in events:
+                samples[v].append(E.elapsed_ms(a, b) * 1000.0 / steps)
                 E.free(a, b)
-    us = sorted(samples)
-    return {"us": float(np.median(us)), "min": us[0], "max": us[-1], "spacer": nspace,
-            "launches": warmup + 16 + (2 if use_graph else 1) * repeats *
-                        (nspace + steps + (TAIL_LAUNCHES if use_graph else 0))}
-
-
-def time_producer(prod, steps, warmup, use_graph, torch, stream, floor=False, repeats=REPEATS):
-    """time_launches over a producer's buffer sets; floor=True times the
-    memory-only counterparts on the same buffers instead."""
-    return time_launches(torch, stream, prod.launch_floor if floor else prod.launch, prod.sets,
-                         steps, warmup, use_graph, repeats)
+    out = []
+    for v in range(nv):
+        us = sorted(samples[v])
+        out.append({"us": float(np.median(us)), "min": us[0], "max": us[-1], "spacer": spacers[v],
+                    "launches": warmup + 16 + (2 if use_graph else 1) * repeats *
+                                (spacers[v] + steps + (TAIL_LAUNCHES if use_graph else 0))})
+    return out
 
 
 class CopyCeiling:
@@ -830,10 +850,11 @@ def floor_sweep(torch, alnp, inputs, F, stream, steps, warmup, use_graph, repeat
         d = inputs.make("ptok", rows=rows, dim=dim)
         nbytes = algorithmic_bytes("ptok", d)
         prod = Producer("ptok_sweep", d, sets_for(nbytes, True), torch, alnp, F)
-        k = time_producer(prod, steps, warmup, use_graph, torch, stream, repeats=repeats)
-        f = time_producer(prod, steps, warmup, use_graph, torch, stream, floor=True, repeats=repeats)
         cp = CopyCeiling(nbytes, True, torch, F)
-        c = time_launches(torch, stream, cp.launch, cp.sets, steps, warmup, use_graph, repeats)
+        k, f, c = time_interleaved(torch, stream, [(prod.launch, prod.sets),
+                                                   (prod.launch_floor, prod.sets),
+                                                   (cp.launch, cp.sets)],
+                                   steps, warmup, use_graph, repeats)
         row = {"rows": rows, "bytes": nbytes, "kernel_us": round(k["us"], 3),
                "floor_us": round(f["us"], 3), "copy_us": round(c["us"], 3),
                "kernel_frac_of_peak": round(nbytes / k["us"] / 1e3 / HBM_PEAK_GBS, 4),
@@ -843,14 +864,17 @@ def floor_sweep(torch, alnp, inputs, F, stream, steps, warmup, use_graph, repeat
         print(f"# sweep {rows}x{dim}: kernel {row['kernel_us']} us, floor {row['floor_us']} us, "
               f"copy {row['copy_us']} us", file=sys.stderr, flush=True)
         if rows == 2520:
-            for waves, vpt in SWEEP_SHAPES:
-                def launch(i, h, prod=prod, waves=waves, vpt=vpt):
+            def shape_launch(waves, vpt):
+                def launch(i, h):
                     fn, args = prod.floor_calls[i % prod.sets]
                     st = F.alnp_floor_rows_shape(*args, waves, vpt, h)
                     if st != 0:
                         raise RuntimeError(f"floor shape {waves}x{vpt}: status {st}")
-                t = time_launches(torch, stream, launch, prod.sets, steps, warmup, use_graph,
-                                  repeats)
+                return launch
+            ts = time_interleaved(torch, stream, [(shape_launch(w, v), prod.sets)
+                                                  for w, v in SWEEP_SHAPES],
+                                  steps, warmup, use_graph, repeats)
+            for (waves, vpt), t in zip(SWEEP_SHAPES, ts):
                 out["shapes"].append({"waves": waves, "vpt": vpt, "us": round(t["us"], 3),
                                       "frac_of_peak": round(nbytes / t["us"] / 1e3 / HBM_PEAK_GBS, 4)})
                 print(f"# shape {waves}x{vpt}: {t['us']:.3f} us", file=sys.stderr, flush=True)
@@ -930,30 +954,36 @@ def main():
             print(f"# timing {name} {mode}: {sets} buffer sets, {a.steps} steps x {repeats}",
                   file=sys.stderr, flush=True)
             prod = Producer(name, d, sets, torch, alnp, F if cold else None)
-            t = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, repeats=repeats)
+            # The producer, its memory-only floor and a plain copy of the same
+            # bytes, their windows interleaved (time_interleaved).
+            variants = [(prod.launch, sets)]
+            if prod.floor_calls:
+                variants.append((prod.launch_floor, sets))
+            cp = CopyCeiling(nbytes, True, torch, F) if cold and F is not None else None
+            if cp is not None:
+                variants.append((cp.launch, cp.sets))
+            res = time_interleaved(torch, stream, variants, a.steps, a.warmup, use_graph, repeats)
+            t = res[0]
+            f = res[1] if prod.floor_calls else None
+            c = res[-1] if cp is not None else None
             print(f"# launches {name} {mode} producer: warmup {a.warmup}, burst 16, spacer "
                   f"{t['spacer']}, steps {a.steps}, tail {TAIL_LAUNCHES if use_graph else 0}, "
-                  f"repeats {repeats}, graph {int(use_graph)}, total {t['launches']}",
+                  f"repeats {repeats}, graph {int(use_graph)}, total {t['launches']}, "
+                  f"interleaved with {len(variants) - 1} other series",
                   file=sys.stderr, flush=True)
             rec = rounded(t)
             rec["spacer_launches"] = t["spacer"]
             rec.update({"gbs": round(nbytes / t["us"] / 1e3, 1), "sets": sets,
                         "footprint_mb": round(sets * nbytes / 2**20, 1)})
-            if prod.floor_calls:
-                f = time_producer(prod, a.steps, a.warmup, use_graph, torch, stream, floor=True,
-                                  repeats=repeats)
+            if f is not None:
                 rec["floor_us"] = round(f["us"], 3)
                 rec["floor_us_range"] = [round(f["min"], 3), round(f["max"], 3)]
                 rec["floor_frac_of_peak"] = round(nbytes / f["us"] / 1e3 / HBM_PEAK_GBS, 4)
                 rec["frac_of_floor"] = round(f["us"] / t["us"], 4)
-            del prod
-            if cold and F is not None:
-                cp = CopyCeiling(nbytes, True, torch, F)
-                c = time_launches(torch, stream, cp.launch, cp.sets, a.steps, a.warmup, use_graph,
-                                  repeats)
+            if c is not None:
                 rec["copy_us"] = round(c["us"], 3)
                 rec["copy_frac_of_peak"] = round(cp.nbytes / c["us"] / 1e3 / HBM_PEAK_GBS, 4)
-                del cp
+            del prod, cp
             r[mode] = rec
             torch.cuda.empty_cache()
         note = ""
