@@ -382,12 +382,17 @@ class HipEvents:
         if getattr(self, "_graphs_ready", False):
             return H
         vp, pvp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)
+        psz, sz = ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t
         sigs = {"hipStreamBeginCapture": [vp, ctypes.c_int],
                 "hipStreamEndCapture": [vp, pvp],
-                "hipGraphCreate": [pvp, ctypes.c_uint],
-                "hipGraphAddChildGraphNode": [pvp, vp, pvp, ctypes.c_size_t, vp],
-                "hipGraphAddEventRecordNode": [pvp, vp, pvp, ctypes.c_size_t, vp],
-                "hipGraphInstantiate": [pvp, vp, vp, vp, ctypes.c_size_t],
+                "hipGraphClone": [pvp, vp],
+                "hipGraphGetNodes": [vp, pvp, psz],
+                "hipGraphGetRootNodes": [vp, pvp, psz],
+                "hipGraphNodeGetDependentNodes": [vp, pvp, psz],
+                "hipGraphRemoveDependencies": [vp, pvp, pvp, sz],
+                "hipGraphAddDependencies": [vp, pvp, pvp, sz],
+                "hipGraphAddEventRecordNode": [pvp, vp, pvp, sz, vp],
+                "hipGraphInstantiate": [pvp, vp, vp, vp, sz],
                 "hipGraphLaunch": [vp, vp],
                 "hipGraphExecDestroy": [vp],
                 "hipGraphDestroy": [vp]}
@@ -418,29 +423,72 @@ class HipEvents:
         self._ok(st, "hipStreamEndCapture")
         return g
 
-    def window_graph(self, spacer, timed, tail, t0, t1):
-        """One executable graph: spacer -> record t0 -> timed -> record t1 ->
-        tail (each a captured graph, cloned into a child node).  The graph
-        launch's own start-up cost falls before the spacer, outside the
-        window between the two event nodes."""
+    def _chain(self, g):
+        """The nodes of a captured single-stream graph in launch order; it
+        must be one chain (each node depends on the one before)."""
         H = self._graph_api()
-        top = ctypes.c_void_p()
-        self._ok(H.hipGraphCreate(ctypes.byref(top), 0), "hipGraphCreate")
-        prev = None
-        for kind, obj in (("child", spacer), ("event", t0), ("child", timed), ("event", t1),
-                          ("child", tail)):
-            node = ctypes.c_void_p()
-            deps, ndeps = (ctypes.byref(prev), 1) if prev is not None else (None, 0)
-            if kind == "child":
-                self._ok(H.hipGraphAddChildGraphNode(ctypes.byref(node), top, deps, ndeps, obj),
-                         "hipGraphAddChildGraphNode")
-            else:
-                self._ok(H.hipGraphAddEventRecordNode(ctypes.byref(node), top, deps, ndeps, obj),
-                         "hipGraphAddEventRecordNode")
-            prev = node
-        ex = ctypes.c_void_p()
-        self._ok(H.hipGraphInstantiate(ctypes.byref(ex), top, None, None, 0), "hipGraphInstantiate")
-        H.hipGraphDestroy(top)     # the child nodes hold copies of the parts
+        vp = ctypes.c_void_p
+        n = ctypes.c_size_t(0)
+        self._ok(H.hipGraphGetNodes(g, None, ctypes.byref(n)), "hipGraphGetNodes")
+        total = n.value
+        n = ctypes.c_size_t(0)
+        self._ok(H.hipGraphGetRootNodes(g, None, ctypes.byref(n)), "hipGraphGetRootNodes")
+        if n.value != 1:
+            raise RuntimeError(f"captured graph has {n.value} root nodes, not one chain")
+        root = (vp * 1)()
+        self._ok(H.hipGraphGetRootNodes(g, root, ctypes.byref(n)), "hipGraphGetRootNodes")
+        nodes = [root[0]]
+        nxt = (vp * 1)()
+        while True:
+            n = ctypes.c_size_t(0)
+            self._ok(H.hipGraphNodeGetDependentNodes(nodes[-1], None, ctypes.byref(n)),
+                     "hipGraphNodeGetDependentNodes")
+            if n.value == 0:
+                break
+            if n.value != 1:
+                raise RuntimeError("captured graph is not one chain")
+            self._ok(H.hipGraphNodeGetDependentNodes(nodes[-1], nxt, ctypes.byref(n)),
+                     "hipGraphNodeGetDependentNodes")
+            nodes.append(nxt[0])
+        if len(nodes) != total:
+            raise RuntimeError(f"captured graph is not one chain ({len(nodes)} of {total} nodes)")
+        return nodes
+
+    def _splice_event(self, g, a, b, ev):
+        """Replace the edge a -> b of graph g by a -> record(ev) -> b."""
+        H = self._graph_api()
+        vp = ctypes.c_void_p
+        fa, tb = (vp * 1)(a), (vp * 1)(b)
+        self._ok(H.hipGraphRemoveDependencies(g, fa, tb, 1), "hipGraphRemoveDependencies")
+        node = vp()
+        self._ok(H.hipGraphAddEventRecordNode(ctypes.byref(node), g, fa, 1, ev),
+                 "hipGraphAddEventRecordNode")
+        self._ok(H.hipGraphAddDependencies(g, (vp * 1)(node), tb, 1), "hipGraphAddDependencies")
+
+    def window_graph(self, seq, launches, nspace, steps, t0, t1):
+        """One executable graph from `seq`, a captured chain of `launches`
+        calls (spacer, then the timed calls, then a tail): a copy of it
+        with an event-record node for t0 spliced in before the first timed
+        call's kernels and one for t1 after the last timed call's.  One flat
+        chain: nesting the three parts as child graphs instead cost about 4
+        us per window on MI355X.  The graph launch's own start-up cost falls
+        before the spacer, outside the window between the two event nodes."""
+        H = self._graph_api()
+        g = ctypes.c_void_p()
+        self._ok(H.hipGraphClone(ctypes.byref(g), seq), "hipGraphClone")
+        try:
+            nodes = self._chain(g)
+            per, rem = divmod(len(nodes), launches)
+            if rem or per == 0:
+                raise RuntimeError(f"{len(nodes)} graph nodes for {launches} calls")
+            first, last = per * nspace, per * (nspace + steps) - 1
+            self._splice_event(g, nodes[first - 1], nodes[first], t0)
+            self._splice_event(g, nodes[last], nodes[last + 1], t1)
+            ex = ctypes.c_void_p()
+            self._ok(H.hipGraphInstantiate(ctypes.byref(ex), g, None, None, 0),
+                     "hipGraphInstantiate")
+        finally:
+            H.hipGraphDestroy(g)
         return ex
 
     def free_captured(self, *graphs):
@@ -519,9 +567,9 @@ def time_interleaved(torch, stream, variants, steps, warmup, use_graph, repeats=
     all the others, and the GPU has been under steady load for a while when
     the window opens.
 
-    With a graph (the default), each window is one executable graph: the
-    spacer, an event-record node, the `steps` timed launches, a second
-    event-record node and a short tail.  The cost of starting a graph
+    With a graph (the default), each window is one executable graph, a
+    single captured chain: the spacer, an event-record node, the `steps`
+    timed launches, a second event-record node and a short tail.  The cost of starting a graph
     launch (several microseconds on this runtime, paid once per launch
     however many kernels the graph holds) then falls before the spacer,
     outside the window, which holds exactly the timed launches.  All
@@ -557,13 +605,15 @@ def time_interleaved(torch, stream, variants, steps, warmup, use_graph, repeats=
             cap = torch.cuda.Stream()
             windows = []                          # per variant: [(exec, t0, t1)] * repeats
             for (launch, _), nspace in zip(variants, spacers):
-                parts = [E.capture(cap, launch, r) for r in
-                         (range(nspace), range(steps), range(steps, steps + TAIL_LAUNCHES))]
+                idx = (list(range(nspace)) + list(range(steps)) +
+                       list(range(steps, steps + TAIL_LAUNCHES)))
+                seq = E.capture(cap, lambda k, hh, launch=launch, idx=idx: launch(idx[k], hh),
+                                range(len(idx)))
                 ws = []
                 for _ in range(repeats):
                     t0, t1 = E.new(), E.new()
-                    ws.append((E.window_graph(*parts, t0, t1), t0, t1))
-                E.free_captured(*parts)
+                    ws.append((E.window_graph(seq, len(idx), nspace, steps, t0, t1), t0, t1))
+                E.free_captured(seq)
                 windows.append(ws)
             for ws in windows:                    # upload, untimed
                 for ex, _, _ in ws:
