@@ -120,9 +120,11 @@ void orc_adaln_fp4_modfp8(const uint16_t* x, const uint8_t* scale_fp8,
                           float eps, int64_t rows, int64_t dim, uint8_t* packed,
                           uint8_t* sf, float* mean, float* rstd, float* b);
 
-/* 128x4 tiled ("swizzled") block-scale layout -- parity unpinned: the pages
- * name the layout but do not define it; this is the tiled layout NVIDIA
- * documents for block-scaled GEMM operands (see the function comment).
+/* 128x4 tiled ("swizzled") block-scale layout.  The pages name the layout
+ * but do not define it; this is the tiled layout NVIDIA documents for
+ * block-scaled GEMM operands (see the function comment).  The tests pin it
+ * byte for byte to PyTorch's own implementation of that documented layout;
+ * agreement with the pages' kernels' bytes cannot be checked.
  * cols = dim / 16 scale columns. */
 int64_t orc_sf_swizzled_size(int64_t rows, int64_t cols);
 int64_t orc_sf_swizzled_offset(int64_t r, int64_t c, int64_t cols);
