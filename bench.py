@@ -10,10 +10,11 @@ step.  Launches are replayed from a HIP graph (the pages' graph method:
 several launches per graph, time / launches).
 
 The other producers (broadcast and table FP8, LN -> FP8, LN -> FP4,
-six-way modulation, RMSNorm modulation, and the MXFP8 / MXFP4 outputs) are
-timed the same way at their workload sizes and reported under "rows", each
-beside its memory-only floor; the headline JSON line is the per-token FP8
-one.
+six-way modulation, RMSNorm modulation, the MXFP8 / MXFP4 outputs, the
+modfp8 and AWQ FP8 forms, AdaLN -> FP4 with row-major and with tiled modfp8
+scales, and the residual gate) are timed the same way at their workload
+sizes and reported under "rows", each beside its memory-only floor; the
+headline JSON line is the per-token FP8 one.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--only-headline] [--direct]
@@ -108,8 +109,19 @@ def algorithmic_bytes(name, d):
     if name.startswith("modulation6"):
         p = d["params"]
         return p.nbytes + d["mod"].nbytes + p.size // 6 * 6 * 2
+    if name.startswith("residual"):
+        return 4 * d["residual"].nbytes    # residual, gate, projection in; bf16 out
     x = d["x"]
     rows, dim = x.shape
+    if name.startswith("adaln_fp4"):
+        # x, e2m1 codes, e4m3 block scales (the tiled layout has no padding at
+        # these sizes), and the (dim,) operands: bf16, or e4m3 plus two fp32 scalars
+        ops = 2 * dim + 8 if "modfp8" in name else 2 * dim * 2
+        return x.nbytes + rows * dim // 2 + rows * dim // 16 + ops
+    if name.startswith("modfp8"):
+        return x.nbytes + rows * dim + 4 + 2 * dim + 8   # e4m3 (dim,) operands, two scalars
+    if name.startswith("awq"):
+        return x.nbytes + rows * dim + 4 + 3 * dim * 2   # scale, shift, inv_s (dim,)
     if name.startswith("mxfp8_ptok"):
         return 3 * x.nbytes + rows * dim + rows * dim // 32   # x, scale, shift; e4m3 + E8M0
     if name.startswith("mxfp8_table"):
@@ -191,8 +203,87 @@ class Producer:
                     add_floor((F.alnp_floor_modulation6, (p.data_ptr(), B * S, D, arr)))
             self.outs = lambda i: self.keep[4 * i + 2]
             return
+        if kind == "residual":
+            r0, g0, p0 = bf(d["residual"]), bf(d["gate"]), bf(d["proj"])
+            rows, dim = r0.shape
+            for _ in range(sets):
+                r, g, pj = r0.clone(), g0.clone(), p0.clone()
+                out = torch.empty_like(r)
+                self.keep.append((r, g, pj, out))
+                self.calls.append((self.L.alnp_gated_residual_bf16,
+                                   (r.data_ptr(), g.data_ptr(), pj.data_ptr(), rows, dim, rows,
+                                    out.data_ptr())))
+                # the same bytes in the row floor's shape: three bf16 rows in, one out
+                add_floor((F.alnp_floor_rows, (r.data_ptr(), g.data_ptr(), pj.data_ptr(), dim, rows,
+                                               dim, FLOOR_BF16, out.data_ptr(), None))
+                          if F is not None else None)
+            return
         x0 = bf(d["x"])
         rows, dim = x0.shape
+        u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(dev)
+        if kind in ("modfp8", "adaln") and "scale_fp8" in d:
+            # the floors read two shared bf16 (dim,) vectors in place of the
+            # e4m3 operands (both stay in cache; a few KB either way)
+            dummy = (bf(d["x"][0]), bf(d["x"][1]))
+            self.keep.append(dummy)
+        if name.startswith("adaln_fp4"):
+            swz = "_swz" in name
+            mod8 = "modfp8" in name
+            sf_bytes = self.L.alnp_swizzled_sf_size(rows, dim) if swz else rows * dim // 16
+            for _ in range(sets):
+                x = x0.clone()
+                packed = torch.empty((rows, dim // 2), dtype=torch.uint8, device=dev)
+                sf = torch.empty(sf_bytes, dtype=torch.uint8, device=dev)
+                if mod8:
+                    sc8, sh8 = u8(d["scale_fp8"]), u8(d["shift_fp8"])
+                    sdeq = torch.tensor([d["scale_deq"]], dtype=torch.float32, device=dev)
+                    hdeq = torch.tensor([d["shift_deq"]], dtype=torch.float32, device=dev)
+                    self.keep.append((x, sc8, sh8, sdeq, hdeq, packed, sf))
+                    self.calls.append((self.L.alnp_ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16,
+                                       (x.data_ptr(), sc8.data_ptr(), sh8.data_ptr(), sdeq.data_ptr(),
+                                        hdeq.data_ptr(), d["eps"], rows, dim, packed.data_ptr(),
+                                        sf.data_ptr(), None, None)))
+                    a_ptr, b_ptr = dummy[0].data_ptr(), dummy[1].data_ptr()
+                else:
+                    sc, sh = bf(d["scale"]), bf(d["shift"])
+                    self.keep.append((x, sc, sh, packed, sf))
+                    fn = (self.L.alnp_ada_layer_norm_quant_nvfp4_swizzled_bf16 if swz
+                          else self.L.alnp_ada_layer_norm_quant_nvfp4_bf16)
+                    self.calls.append((fn, (x.data_ptr(), sc.data_ptr(), sh.data_ptr(), d["eps"],
+                                            rows, dim, packed.data_ptr(), sf.data_ptr(), None,
+                                            None)))
+                    a_ptr, b_ptr = sc.data_ptr(), sh.data_ptr()
+                add_floor((F.alnp_floor_rows, (x.data_ptr(), a_ptr, b_ptr, 0, rows, dim,
+                                               FLOOR_NVFP4, packed.data_ptr(), sf.data_ptr()))
+                          if F is not None else None)
+            return
+        if kind in ("modfp8", "awq"):
+            act0 = torch.tensor([d["act_scale"]], dtype=torch.float32, device=dev)
+            for _ in range(sets):
+                x, act = x0.clone(), act0.clone()
+                out = torch.empty((rows, dim), dtype=torch.uint8, device=dev)
+                if kind == "modfp8":
+                    sc8, sh8 = u8(d["scale_fp8"]), u8(d["shift_fp8"])
+                    sdeq = torch.tensor([d["scale_deq"]], dtype=torch.float32, device=dev)
+                    hdeq = torch.tensor([d["shift_deq"]], dtype=torch.float32, device=dev)
+                    self.keep.append((x, act, sc8, sh8, sdeq, hdeq, out))
+                    self.calls.append((self.L.alnp_ada_layer_norm_quant_fp8_modfp8_bf16,
+                                       (x.data_ptr(), sc8.data_ptr(), sh8.data_ptr(),
+                                        sdeq.data_ptr(), hdeq.data_ptr(), act.data_ptr(), d["eps"],
+                                        rows, dim, out.data_ptr(), None, None)))
+                    a_ptr, b_ptr = dummy[0].data_ptr(), dummy[1].data_ptr()
+                else:
+                    sc, sh, isv = bf(d["scale"]), bf(d["shift"]), bf(d["inv_s"])
+                    self.keep.append((x, act, sc, sh, isv, out))
+                    self.calls.append((self.L.alnp_awq_ada_layer_norm_quant_fp8_bf16,
+                                       (x.data_ptr(), sc.data_ptr(), sh.data_ptr(), isv.data_ptr(),
+                                        act.data_ptr(), d["eps"], rows, dim, out.data_ptr(), None,
+                                        None)))
+                    a_ptr, b_ptr = sc.data_ptr(), sh.data_ptr()
+                add_floor((F.alnp_floor_rows, (x.data_ptr(), a_ptr, b_ptr, 0, rows, dim, FLOOR_FP8,
+                                               out.data_ptr(), None))
+                          if F is not None else None)
+            return
         if name.startswith("mxfp8_table"):
             te0, tb0 = bf(d["temb"]), f32(d["table"])
             chunks = d["temb"].shape[1]
@@ -976,7 +1067,9 @@ def main():
     names = [head] if a.only_headline else [
         head, "table_fp8_2520x3072", "bcast_fp8_16x2048", "ln_fp8_2520x3072",
         "ln_fp4_4096x3072", "modulation6_1x5070x3072", "rmsmod_bf16_37810x5376",
-        "mxfp8_ptok_2520x3072", "mxfp8_table_2520x3072", "ln_mxfp4_4096x3072"]
+        "mxfp8_ptok_2520x3072", "mxfp8_table_2520x3072", "ln_mxfp4_4096x3072",
+        "modfp8_fp8_2520x3072", "awq_fp8_2520x3072", "adaln_fp4_4096x3072",
+        "adaln_fp4_swz_modfp8_4096x3072", "residual_bf16_5070x3072"]
     if a.only:
         names = [n for n in a.only.split(",") if n]
     results = {}

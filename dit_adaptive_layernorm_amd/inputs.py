@@ -31,7 +31,8 @@ import torch
 
 # One stream id per tensor role, so that adding a tensor never shifts another.
 STREAM = {"x": 1, "scale": 2, "shift": 3, "temb": 4, "table": 5, "params": 6,
-          "mod": 7, "outlier": 8, "weight": 9, "seg": 10}
+          "mod": 7, "outlier": 8, "weight": 9, "seg": 10, "scale_fp8": 11,
+          "shift_fp8": 12, "inv_s": 13, "gate": 14, "proj": 15}
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -50,6 +51,12 @@ def normal_f32(shape, sigma: float, seed: int, stream: int) -> np.ndarray:
 
 def normal_bf16(shape, sigma: float, seed: int, stream: int) -> np.ndarray:
     return to_bf16_bits(normal_f32(shape, sigma, seed, stream))
+
+
+def to_e4m3_bits(f32: np.ndarray) -> np.ndarray:
+    """Round float32 to e4m3 (OCP float8_e4m3fn) with torch's conversion; uint8 codes."""
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def outlier_bf16(shape, seed: int, stream: int, outlier_stream: int,
@@ -93,6 +100,14 @@ WORKLOADS = {
     "ln_fp4_4096x3072": dict(kind="fp4", rows=4096, dim=3072),
     "rmsmod_bf16_37810x5376": dict(kind="rmsmod", rows=37810, dim=5376, segments=3,
                                    layout="h3"),
+    # the README's further entries, at the shapes above: e4m3 modulation
+    # operands and AWQ smoothing at the per-token size, AdaLN -> FP4 at the FP4
+    # size, and the residual gate at the six-way size (a per-token gate)
+    "modfp8_fp8_2520x3072": dict(kind="modfp8", rows=2520, dim=3072),
+    "awq_fp8_2520x3072": dict(kind="awq", rows=2520, dim=3072),
+    "adaln_fp4_4096x3072": dict(kind="adaln_fp4", rows=4096, dim=3072),
+    "adaln_fp4_swz_modfp8_4096x3072": dict(kind="adaln_fp4_modfp8", rows=4096, dim=3072),
+    "residual_bf16_5070x3072": dict(kind="residual", rows=5070, dim=3072),
 }
 
 # The h3 page's request layout: (first token, end token, modulation row).
@@ -114,9 +129,23 @@ def make(kind: str, seed: int = 0, rows: int = 0, dim: int = 0, chunks: int = 6,
          outliers: bool = True, segments: int = 3, layout: str = "random") -> dict:
     """Inputs for one producer at any shape, same distributions as above.
 
-    kind: "ln" | "bcast" | "ptok" | "table" | "fp4" | "mod6" | "rmsmod".
+    kind: "ln" | "bcast" | "ptok" | "table" | "fp4" | "mod6" | "rmsmod", or the
+    variants "modfp8" | "awq" | "adaln_fp4" | "adaln_fp4_modfp8" | "residual".
     """
     s = STREAM
+    if kind == "residual":
+        # residual stream N(0, 1), per-token gate N(0, 0.5), projection N(0, 2)
+        return dict(residual=normal_bf16((rows, dim), 1.0, seed, s["x"]),
+                    gate=normal_bf16((rows, dim), 0.5, seed, s["gate"]),
+                    proj=normal_bf16((rows, dim), 2.0, seed, s["proj"]))
+    if kind in ("adaln_fp4", "adaln_fp4_modfp8"):
+        d = make("fp4", seed=seed, rows=rows, dim=dim, outliers=outliers)
+        if kind == "adaln_fp4":
+            d["scale"] = normal_bf16((dim,), 0.1, seed, s["scale"])
+            d["shift"] = normal_bf16((dim,), 0.1, seed, s["shift"])
+        else:
+            d.update(modfp8_operands(dim, seed))
+        return d
     if kind == "rmsmod":
         w = (normal_f32((dim,), 0.1, seed, s["weight"]) + np.float32(1.0)).astype(np.float32)
         return dict(x=normal_bf16((rows, dim), 1.0, seed, s["x"]), weight=to_bf16_bits(w),
@@ -142,9 +171,29 @@ def make(kind: str, seed: int = 0, rows: int = 0, dim: int = 0, chunks: int = 6,
         d["table"] = normal_f32((chunks, dim), 0.1, seed, s["table"])
         d["shift_idx"] = shift_idx
         d["scale_idx"] = scale_idx
+    elif kind == "modfp8":
+        d.update(modfp8_operands(dim, seed))
+    elif kind == "awq":
+        d["scale"] = normal_bf16((dim,), 0.1, seed, s["scale"])
+        d["shift"] = normal_bf16((dim,), 0.1, seed, s["shift"])
+        # per-channel smoothing factors in [0.5, ~2.5)
+        d["inv_s"] = to_bf16_bits(np.abs(normal_f32((dim,), 0.5, seed, s["inv_s"])) + np.float32(0.5))
     elif kind != "ln":
         raise ValueError(kind)
     return d
+
+
+# fp32 dequantization scalars of the e4m3 modulation operands
+MODFP8_DEQ = (0.5, 0.25)
+
+
+def modfp8_operands(dim: int, seed: int) -> dict:
+    """e4m3 (dim,) scale / shift codes of N(0, 0.3) draws and their fp32
+    dequantization scalars (MODFP8_DEQ), so the operands are N(0, 0.15) and
+    N(0, 0.075) in value."""
+    return dict(scale_fp8=to_e4m3_bits(normal_f32((dim,), 0.3, seed, STREAM["scale_fp8"])),
+                shift_fp8=to_e4m3_bits(normal_f32((dim,), 0.3, seed, STREAM["shift_fp8"])),
+                scale_deq=MODFP8_DEQ[0], shift_deq=MODFP8_DEQ[1])
 
 
 def workload(name: str, seed: int = 0) -> dict:
