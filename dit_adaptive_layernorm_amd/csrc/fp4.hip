@@ -70,9 +70,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_fp4_rows(Fp4Args a)
     const int dim = a.dim;
     const int nvec = dim >> 3;  // even, since dim % 16 == 0
     const int cols = dim >> 4;
-    const int64_t row = grid_row();
+    int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
+    if (SWZ && (a.rows & 255) == 0) {
+        // In the tiled layout a 128-byte line of scales holds 4 bytes from
+        // each of 32 rows (equal r div 128 and (r mod 32) div 8).  Workgroups
+        // go to the eight XCDs in turn, so workgroup w takes the row that
+        // puts those 32 rows on one XCD, whose L2 then assembles each line
+        // whole instead of eight L2s writing parts of it.  A bijection on
+        // [0, rows) for rows a multiple of 256: w -> XCD x = w mod 8, its
+        // k = w div 8 -> line group g = x + 8 (k div 32), member m = k mod 32.
+        const int64_t x = row & 7, k = row >> 3;
+        const int64_t g = x + 8 * (k >> 5), m = k & 31;
+        row = (g >> 2) * 128 + 32 * (m >> 3) + 8 * (g & 3) + (m & 7);
+    }
     // The encode factors 1 / s, staged from the compile-time table into LDS
     // (requested here, written once the row loads are in flight).
     const float recip0 = !MX && t < 128 ? kE4m3Recip.v[t] : 0.f;

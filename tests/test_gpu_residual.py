@@ -1,7 +1,8 @@
 """Parity of the residual-gate step with the oracle, bit-exact, through the
-C ABI: per-token and broadcast gates, vector and scalar kernels, in-place
-update, and a full Wan-size residual stream gated by a six-way producer
-output."""
+C ABI: per-token gates (row kernel in every row shape, and the slot kernel
+above the row shapes' largest dim) and broadcast gates (slot kernel), the
+scalar fallback, in-place update, and a full Wan-size residual stream gated
+by a six-way producer output."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +23,8 @@ def make(rows, dim, seed, bcast):
 
 @pytest.mark.parametrize("bcast", [False, True])
 @pytest.mark.parametrize("rows,dim", [(1, 8), (3, 3072), (5, 1536), (7, 1152), (130, 512),
-                                      (2, 6), (3, 1030), (4, 12000), (1, 7)])
+                                      (2, 6), (3, 1030), (4, 12000), (1, 7), (2, 32768),
+                                      (1, 40000), (3, 24), (9, 5376)])
 def test_shapes(orc, bcast, rows, dim):
     print(f"gated residual bcast={bcast} rows={rows} dim={dim}", flush=True)
     res, gate, proj = make(rows, dim, rows + dim, bcast)

@@ -311,3 +311,99 @@ def test_adaln_fp4_unaligned_fallback(orc):
     packed, sf = alnp.ada_layer_norm_quant_nvfp4_bf16(x, dev_bf16(d["scale"]), dev_bf16(d["shift"]))
     rp, rs, _, _, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"])
     fp4_check(host_u8(packed), host_u8(sf), rp, rs, "adaln fp4 unaligned")
+
+
+# ---- launch-time choices that must not change bytes ----------------------------------
+
+def _shared_operand_call(kind, mx, x, d):
+    """One call of a shared-operand form; returns (codes, mx scales or None,
+    row_mean, row_rstd) on the host."""
+    rows = x.shape[0]
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    sc, sh = dev_bf16(d["scale"]), dev_bf16(d["shift"])
+    s8, h8 = dev_u8_as_fp8(d["scale_fp8"]), dev_u8_as_fp8(d["shift_fp8"])
+    inv_s = dev_bf16(d["inv_s"])
+    st = dict(row_mean=mean, row_rstd=rstd)
+    if mx:
+        if kind == "bcast":
+            o, s = alnp.ada_layer_norm_quant_mxfp8_bf16(x, sc, sh, **st)
+        elif kind == "modfp8":
+            o, s = alnp.ada_layer_norm_quant_mxfp8_modfp8_bf16(x, s8, h8, scalar(0.75), scalar(1.5), **st)
+        else:
+            o, s = alnp.awq_ada_layer_norm_quant_mxfp8_bf16(x, sc, sh, inv_s, **st)
+        return host_u8(o), host_u8(s), mean.cpu().numpy(), rstd.cpu().numpy()
+    if kind == "bcast":
+        o = alnp.ada_layer_norm_quant_fp8_bf16(x, sc, sh, act(), **st)
+    elif kind == "modfp8":
+        o = alnp.ada_layer_norm_quant_fp8_modfp8_bf16(x, s8, h8, scalar(0.75), scalar(1.5), act(), **st)
+    else:
+        o = alnp.awq_ada_layer_norm_quant_fp8_bf16(x, sc, sh, inv_s, act(), **st)
+    return host_u8(o), None, mean.cpu().numpy(), rstd.cpu().numpy()
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("kind", ["bcast", "modfp8", "awq"])
+def test_shared_operand_forms_same_bytes_across_the_row_threshold(kind, mx):
+    """From 512 rows the broadcast, modfp8 and AWQ forms form (1 + scale) and
+    shift before the row arrives; smaller calls keep x first.  A 1030-row
+    call and calls of at most 511 rows give the same codes, scales and row
+    statistics."""
+    print(f"shared-operand threshold kind={kind} mx={mx}", flush=True)
+    rows, dim = 1030, 3072
+    d = modfp8_inputs(rows, dim, seed=41)
+    d["inv_s"] = inputs.to_bf16_bits(np.abs(inputs.normal_f32((dim,), 0.5, 41, 11)) + 0.5)
+    x = dev_bf16(d["x"])
+    full = _shared_operand_call(kind, mx, x, d)
+    for r0, bs in ((0, 511), (511, 511), (1022, 8), (300, 1)):
+        part = _shared_operand_call(kind, mx, x[r0:r0 + bs], d)
+        for p, f in zip(part, full):
+            if p is None:
+                continue
+            if p.ndim == 2:
+                assert np.array_equal(p, f[r0:r0 + bs]), (kind, mx, r0, bs)
+            else:
+                assert np.array_equal(p, f[r0:r0 + bs]), (kind, mx, r0, bs, "stats")
+
+
+@pytest.mark.parametrize("mod", ["ln", "bcast", "modfp8"])
+@pytest.mark.parametrize("rows,dim", [(512, 3072), (768, 1536), (256, 80)])
+def test_fp4_swizzled_row_grouping(orc, mod, rows, dim):
+    """With rows a multiple of 256 the tiled-scale entries hand rows to
+    workgroups in an XCD-grouped order; codes, tiled scales and row
+    statistics must match the oracle and the row-major entries byte for
+    byte."""
+    print(f"fp4 swizzled grouping mod={mod} rows={rows} dim={dim}", flush=True)
+    d = modfp8_inputs(rows, dim, seed=rows + dim)
+    cols = dim // 16
+    x = dev_bf16(d["x"])
+    st = lambda: (torch.empty(rows, dtype=torch.float32, device="cuda"),
+                  torch.empty(rows, dtype=torch.float32, device="cuda"))
+    (m1, r1), (m2, r2) = st(), st()
+    if mod == "ln":
+        p1, s1 = alnp.layer_norm_no_affine_quant_nvfp4_swizzled_bf16(x, row_mean=m1, row_rstd=r1)
+        p2, s2 = alnp.layer_norm_no_affine_quant_nvfp4_bf16(x, row_mean=m2, row_rstd=r2)
+        rp, rs, rm, rr, _ = orc.ln_fp4(d["x"])
+    elif mod == "bcast":
+        sc, sh = dev_bf16(d["scale"]), dev_bf16(d["shift"])
+        p1, s1 = alnp.ada_layer_norm_quant_nvfp4_swizzled_bf16(x, sc, sh, row_mean=m1, row_rstd=r1)
+        p2, s2 = alnp.ada_layer_norm_quant_nvfp4_bf16(x, sc, sh, row_mean=m2, row_rstd=r2)
+        rp, rs, rm, rr, _ = orc.adaln_fp4(d["x"], d["scale"], d["shift"])
+    else:
+        p1, s1 = alnp.ada_layer_norm_quant_nvfp4_swizzled_modfp8_bf16(
+            x, dev_u8_as_fp8(d["scale_fp8"]), dev_u8_as_fp8(d["shift_fp8"]), scalar(0.75),
+            scalar(1.5), row_mean=m1, row_rstd=r1)
+        p2, s2 = None, None
+        rp, rs, rm, rr, _ = orc.adaln_fp4_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5)
+    got = host_u8(s1)
+    pos = swizzled_positions(orc, rows, cols)
+    fp4_check(host_u8(p1), got[pos], rp, rs, f"grouped swizzled {mod} {rows}x{dim}")
+    for r in range(rows):
+        for c in range(cols, -(-cols // 4) * 4):
+            assert got[orc.sf_swizzled_offset(r, c, cols)] == 0
+    assert_stats_close(m1.cpu().numpy(), r1.cpu().numpy(), rm, rr)
+    if p2 is not None:
+        assert np.array_equal(host_u8(p1), host_u8(p2))
+        assert np.array_equal(got[pos], host_u8(s2))
+        assert np.array_equal(m1.cpu().numpy(), m2.cpu().numpy())
+        assert np.array_equal(r1.cpu().numpy(), r2.cpu().numpy())
