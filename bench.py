@@ -165,7 +165,7 @@ def floor_lib():
 
 
 # out_kind of alnp_floor_rows
-FLOOR_FP8, FLOOR_NVFP4, FLOOR_BF16, FLOOR_MXFP8, FLOOR_MXFP4 = 0, 1, 2, 3, 4
+FLOOR_FP8, FLOOR_NVFP4, FLOOR_BF16, FLOOR_MXFP8, FLOOR_MXFP4, FLOOR_NVFP4_TILED = 0, 1, 2, 3, 4, 5
 
 
 class Producer:
@@ -254,7 +254,8 @@ class Producer:
                                             None)))
                     a_ptr, b_ptr = sc.data_ptr(), sh.data_ptr()
                 add_floor((F.alnp_floor_rows, (x.data_ptr(), a_ptr, b_ptr, 0, rows, dim,
-                                               FLOOR_NVFP4, packed.data_ptr(), sf.data_ptr()))
+                                               FLOOR_NVFP4_TILED if swz else FLOOR_NVFP4,
+                                               packed.data_ptr(), sf.data_ptr()))
                           if F is not None else None)
             return
         if kind in ("modfp8", "awq"):

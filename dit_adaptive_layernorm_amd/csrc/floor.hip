@@ -23,7 +23,18 @@ enum FloorOut : int {
     kOutBf16 = 2,   // 2 bytes per element
     kOutMxfp8 = 3,  // 1 byte per element + dim/32 scale bytes per row
     kOutMxfp4 = 4,  // dim/2 bytes of codes + dim/32 scale bytes per row
+    kOutNvfp4Tiled = 5,  // as kOutNvfp4, scales in the 128x4 tiled layout, rows in
+                         // the tiled FP4 producers' XCD-grouped order
 };
+
+// Byte offset of scale (r, c) in the 128x4 tiled layout (the producers'
+// layout, restated here so that this library stays self-contained).
+__device__ __forceinline__ int64_t tiled_offset(int64_t r, int c, int cols)
+{
+    const int64_t tile = (r >> 7) * ((cols + 3) >> 2) + (c >> 2);
+    const int rr = (int)(r & 127);
+    return tile * 512 + (rr & 31) * 16 + (rr >> 5) * 4 + (c & 3);
+}
 
 struct FloorRowArgs {
     const uint16_t* x;
@@ -41,9 +52,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_floor_rows(FloorRowArgs f)
 {
     constexpr int T = WAVES * 64;
     const int t = threadIdx.x;
-    const int64_t row = grid_row();
+    int64_t row = grid_row();
     if (row >= f.rows)
         return;
+    if (OUT == kOutNvfp4Tiled && (f.rows & 255) == 0) {
+        const int64_t x = row & 7, k = row >> 3;
+        const int64_t g = x + 8 * (k >> 5), m = k & 31;
+        row = (g >> 2) * 128 + 32 * (m >> 3) + 8 * (g & 3) + (m & 7);
+    }
     const int dim = f.dim;
     const int nvec = dim >> 3;
     const bool stream_ab = f.ab_stride != 0;
@@ -85,6 +101,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_floor_rows(FloorRowArgs f)
             st_stream(f.out + row * (dim >> 1) + (int64_t)i * 4, w.x ^ w.y ^ w.z ^ w.w);
             if (OUT == kOutNvfp4 && (i & 1) == 0)
                 f.scales[row * (dim >> 4) + (i >> 1)] = (uint8_t)w.x;
+            if (OUT == kOutNvfp4Tiled && (i & 1) == 0)
+                f.scales[tiled_offset(row, i >> 1, dim >> 4)] = (uint8_t)w.x;
             if (OUT == kOutMxfp4 && (i & 3) == 0)
                 f.scales[row * (dim >> 5) + (i >> 2)] = (uint8_t)w.x;
         }
@@ -194,7 +212,9 @@ using namespace alnp;
 //   (ab_stride 0: one (dim,) vector shared by every row, read through cache).
 //   out_kind: 0 = 1 B/element; 1 = NVFP4 (dim/2 code bytes per row, scales
 //   (rows, dim/16)); 2 = bf16 (rows, dim); 3 = MXFP8 (1 B/element, scales
-//   (rows, dim/32)); 4 = MXFP4 (dim/2 code bytes, scales (rows, dim/32)).
+//   (rows, dim/32)); 4 = MXFP4 (dim/2 code bytes, scales (rows, dim/32));
+//   5 = NVFP4 with scales in the 128x4 tiled layout (dim a multiple of 64),
+//   rows in the tiled FP4 producers' order.
 // Returns 0, or -1 for a shape or pointer the row kernels do not take (dim
 // not a multiple of 32, rows longer than the register-resident row shapes,
 // unaligned pointers), -2 for an unknown out_kind, -6 for a launch failure.
@@ -242,7 +262,8 @@ static int floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b, i
         return -1;
     if (!aligned16(x) || !aligned16(out) || (a && !aligned16(a)) || (b && !aligned16(b)))
         return -1;
-    const bool want_scales = out_kind == kOutNvfp4 || out_kind == kOutMxfp8 || out_kind == kOutMxfp4;
+    const bool want_scales = out_kind == kOutNvfp4 || out_kind == kOutMxfp8 ||
+                             out_kind == kOutMxfp4 || out_kind == kOutNvfp4Tiled;
     if (want_scales && !scales)
         return -1;
     if (rs.vpt == 0)
@@ -256,6 +277,11 @@ static int floor_rows(const uint16_t* x, const uint16_t* a, const uint16_t* b, i
     case kOutBf16: e = launch_floor_nin<kOutBf16>(f, nin, rs, stream); break;
     case kOutMxfp8: e = launch_floor_nin<kOutMxfp8>(f, nin, rs, stream); break;
     case kOutMxfp4: e = launch_floor_nin<kOutMxfp4>(f, nin, rs, stream); break;
+    case kOutNvfp4Tiled:
+        if (dim % 64 != 0)
+            return -1;  // whole tiles of scale columns only
+        e = launch_floor_nin<kOutNvfp4Tiled>(f, nin, rs, stream);
+        break;
     default: return -2;
     }
     return e == hipSuccess ? 0 : -6;

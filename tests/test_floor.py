@@ -12,7 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PATH = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "libalnp_floor.so")
-FP8, NVFP4, BF16, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+FP8, NVFP4, BF16, MXFP8, MXFP4, NVFP4_TILED = 0, 1, 2, 3, 4, 5
 
 
 def floor_lib():
@@ -41,8 +41,9 @@ def test_floor_library_exports_and_rejects_bad_arguments():
     assert F.alnp_floor_rows(A + 4, None, None, 0, 4, 64, FP8, B, None, None) == -1
     assert F.alnp_floor_rows(A, None, A, 0, 4, 64, FP8, B, None, None) == -1     # b without a
     assert F.alnp_floor_rows(A, None, None, -1, 4, 64, FP8, B, None, None) == -1
-    for kind in (NVFP4, MXFP8, MXFP4):
+    for kind in (NVFP4, MXFP8, MXFP4, NVFP4_TILED):
         assert F.alnp_floor_rows(A, None, None, 0, 4, 64, kind, B, None, None) == -1
+    assert F.alnp_floor_rows(A, None, None, 0, 4, 96, NVFP4_TILED, B, B, None) == -1  # dim % 64
     assert F.alnp_floor_rows(A, None, None, 0, 4, 64, 9, B, None, None) == -2
     assert F.alnp_floor_rows(A, None, None, 0, 4, 1 << 21, FP8, B, None, None) == -1
     outs = (ctypes.c_void_p * 6)(*([B] * 6))
@@ -141,6 +142,43 @@ def test_floor_rows_store_the_producers_bytes(kind, nin, stride_kind, rows, dim)
     assert np.array_equal(got, np.ascontiguousarray(want).view(np.uint8).reshape(-1))
     if want_s is not None:
         assert np.array_equal(scales.cpu().numpy(), want_s.reshape(-1))
+
+
+def tiled_offset(r, c, cols):
+    """The 128x4 tiled scale layout: 512-byte tiles of 128 rows x 4 columns,
+    tile-row-major; (r mod 32) picks a 16-byte unit, (r div 32) mod 4 the
+    4-byte group in it, c mod 4 the byte."""
+    tile = (r // 128) * ((cols + 3) // 4) + c // 4
+    return tile * 512 + (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,dim", [(5, 3072), (256, 3072), (512, 128)])
+def test_floor_rows_tiled_scales(rows, dim):
+    """The tiled-scale floor stores the NVFP4 floor's codes, and its scale
+    bytes at their tiled positions (rows a multiple of 256 take the XCD-grouped
+    order, which must not change which bytes land where)."""
+    import torch
+    F = floor_lib()
+    print(f"floor rows tiled {rows}x{dim}", flush=True)
+    r = np.random.default_rng(rows + dim)
+    x = r.integers(0, 1 << 16, size=(rows, dim), dtype=np.uint16)
+    want, want_rm = expected_rows(NVFP4, x)
+    cols = dim // 16
+    size = -(-rows // 128) * 128 * (-(-cols // 4) * 4)
+    want_s = np.full(size, 0x5A, np.uint8)
+    for rr in range(rows):
+        for c in range(cols):
+            want_s[tiled_offset(rr, c, cols)] = want_rm[rr, c]
+    out = torch.full((want.size,), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((size,), 0x5A, dtype=torch.uint8, device="cuda")
+    x_d = torch.from_numpy(x.view(np.int16)).cuda()
+    st = F.alnp_floor_rows(x_d.data_ptr(), None, None, 0, rows, dim, NVFP4_TILED, out.data_ptr(),
+                           scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), np.ascontiguousarray(want).view(np.uint8).reshape(-1))
+    assert np.array_equal(scales.cpu().numpy(), want_s)
 
 
 @pytest.mark.gpu
