@@ -407,3 +407,26 @@ def test_fp4_swizzled_row_grouping(orc, mod, rows, dim):
         assert np.array_equal(got[pos], host_u8(s2))
         assert np.array_equal(m1.cpu().numpy(), m2.cpu().numpy())
         assert np.array_equal(r1.cpu().numpy(), r2.cpu().numpy())
+
+
+@pytest.mark.parametrize("kind", ["bcast", "modfp8", "awq"])
+@pytest.mark.parametrize("dim", [8, 1152, 1536, 2048, 5376, 6144, 12000])
+def test_shared_operand_forms_ahead_of_the_row_shapes(orc, kind, dim):
+    """600 rows: the operands-ahead path at every row shape it takes (up to
+    three vectors per thread, partial last slots) and the plain path above
+    it, against the oracle."""
+    rows = 600
+    print(f"shared-operand forms ahead kind={kind} dim={dim}", flush=True)
+    d = modfp8_inputs(rows, dim, seed=7 * dim + 5)
+    d["inv_s"] = inputs.to_bf16_bits(np.abs(inputs.normal_f32((dim,), 0.5, dim, 11)) + 0.5)
+    got, _, m, r = _shared_operand_call(kind, False, dev_bf16(d["x"]), d)
+    if kind == "bcast":
+        ref, rm, rr, _ = orc.adaln_fp8_bcast(d["x"], d["scale"], d["shift"], 0.025, threads=8)
+    elif kind == "modfp8":
+        ref, rm, rr, _ = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5,
+                                              0.025, threads=8)
+    else:
+        ref, rm, rr, _ = orc.awq_adaln_fp8(d["x"], d["scale"], d["shift"], d["inv_s"], 0.025,
+                                           threads=8)
+    assert_codes_close(got, ref, e4m3_ordinal, f"{kind} {rows}x{dim}")
+    assert_stats_close(m, r, rm, rr)
