@@ -68,6 +68,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         // shorter.  2520 x 3072 cold: modfp8 7.01 -> 6.77 us, AWQ 7.45 ->
         // 7.33 us (A-B, same box, bit-identical).  Streamed per-row operands
         // (load_streamed below) are requested after the row statistics.
+        // With kPre, the operands that only the output pass reads (the
+        // broadcast shift, AWQ's inv_s) are requested after the mean
+        // instead: every load a CU issues ahead of x holds up the x of its
+        // later rows, and these arrive while the variance is summed.
+        // Broadcast 6.88 -> 6.74 us, AWQ 7.35 -> 7.18 us (A-B, bit-identical;
+        // AWQ's shift and the modfp8 shift measured slower that way).  The
+        // MXFP8 forms, not measured so, keep every operand ahead of x.
+        constexpr bool kLateShift = kPre && !MX && FORM == kBcast;
+        constexpr bool kLateInvS = kPre && !MX && FORM == kAwq;
         uint4 scv[NB], shv[NB];
         uint2 sc8[N8], sh8[N8];
         uint4 isv[NI];
@@ -75,8 +84,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
                 scv[v] = ld_row<false>(a.scale, v * T + t, nvec, !FULL && v == VPT - 1);
-                shv[v] = ld_row<false>(a.shift, v * T + t, nvec, !FULL && v == VPT - 1);
-                if (FORM == kAwq)
+                if (!kLateShift)
+                    shv[v] = ld_row<false>(a.shift, v * T + t, nvec, !FULL && v == VPT - 1);
+                if (FORM == kAwq && !kLateInvS)
                     isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, !FULL && v == VPT - 1);
             }
         } else if (FORM == kModFp8) {
@@ -109,17 +119,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                     }
                 } else {
                     unpack8(scv[v], sc);
-                    unpack8(shv[v], sh);
+                    if (!kLateShift)
+                        unpack8(shv[v], sh);
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     tp[v][e] = 1.0f + sc[e];
-                    hp[v][e] = sh[e];
+                    hp[v][e] = kLateShift ? 0.f : sh[e];
                 }
                 // Keep the compiler from sinking this into the output pass.
                 asm volatile("" : "+v"(tp[v][0]), "+v"(tp[v][1]), "+v"(tp[v][2]), "+v"(tp[v][3]),
                                   "+v"(tp[v][4]), "+v"(tp[v][5]), "+v"(tp[v][6]), "+v"(tp[v][7]));
-                if (FORM != kAwq)
+                if (FORM != kAwq && !kLateShift)
                     asm volatile("" : "+v"(hp[v][0]), "+v"(hp[v][1]), "+v"(hp[v][2]), "+v"(hp[v][3]),
                                       "+v"(hp[v][4]), "+v"(hp[v][5]), "+v"(hp[v][6]), "+v"(hp[v][7]));
             }
@@ -172,6 +183,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         float d[VPT][8];
         const float mean = row_mean<VPT>(xv, a.inv_dim, reduce);
         load_streamed(kAfterMean);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            if (kLateShift)
+                shv[v] = ld_row<false>(a.shift, v * T + t, nvec, !FULL && v == VPT - 1);
+            if (kLateInvS)
+                isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, !FULL && v == VPT - 1);
+        }
         const float rstd = row_rstd<VPT>(xv, tail_ok, mean, a.inv_dim, a.eps, reduce, d);
         load_streamed(kAfterRstd);
 
@@ -187,6 +205,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                     sc[e] = 0.f;
                     sh[e] = 0.f;
                 }
+                if (kLateShift)
+                    unpack8(shv[v], sh);
             } else if (FORM == kModFp8) {
                 // Dequantize: e4m3 value times its fp32 scalar, one rounding.
                 unpack_e4m3x8(sc8[v], sc);
@@ -230,7 +250,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xhat = d[v][e] * rstd;
-                float y = kPre ? (xhat * tp[v][e]) + hp[v][e] : (xhat * (1.0f + sc[e])) + sh[e];
+                float y = kPre ? (xhat * tp[v][e]) + (kLateShift ? sh[e] : hp[v][e])
+                               : (xhat * (1.0f + sc[e])) + sh[e];
                 if (FORM == kAwq)
                     y = y * is[e];  // per-channel smoothing before the static scale
                 q[e] = MX ? y : y * inv;
@@ -263,8 +284,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 // VGPRs per thread, which leaves room for only 2048 of the 2520 rows of the
 // Wan workload on the chip at once; from LDS the kernel keeps the per-token
 // kernel's register budget and reads each table element from L2 once per
-// two rows instead of once per row.  The table loads (L2 hits) are issued
-// before the row loads so that the LDS fill does not wait behind them.
+// two rows instead of once per row.  When the table loads (L2 hits) are
+// issued is set per output format below.
 constexpr int kTableRows = 2;     // rows per workgroup
 // LDS bound: 2 table rows * 8192 * 4 B = 64 KiB.  The row shapes of at most
 // four waves, which this kernel takes, end at dim 7168 (57344 bytes) anyway.
@@ -294,16 +315,29 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     const int64_t row = grid_row() * R + rr;
     const bool valid = row < a.rows;
 
-    // Table rows first: up to 8 float4 per thread in flight, the rest (only
-    // for dims above 4 * 2 * NT ... 8192) loaded after the row operands.
+    // The table rows: up to 8 float4 per thread in flight, the rest (only for
+    // dims above 4 * 2 * NT ... 8192) loaded while they are written to LDS.
+    // Where they are requested depends on the output format (XFIRST below).
     const float4* tsrc = reinterpret_cast<const float4*>(a.table + (int64_t)a.scale_idx * dim);
     const float4* thsrc = reinterpret_cast<const float4*>(a.table + (int64_t)a.shift_idx * dim);
     constexpr int kFirst = 8;
     float4 tv[kFirst];
+    // XFIRST (FP8): the row's x is requested first and the table rows only
+    // once x has landed; they go to LDS before the second reduction, whose
+    // barrier publishes them.  Requested ahead of x, the table loads of the
+    // first workgroups on a CU (24 KiB each, L2 hits) hold up the issue of
+    // the later workgroups' x by microseconds (per-wave timestamps: the
+    // fourth and fifth workgroups of a CU got x 2-4 us after the first
+    // three).  2520 x 3072 cold: 10.97 -> 10.81 us, bit-identical.  MXFP8
+    // keeps the table ahead of x, which measured better there (11.17
+    // against 11.37 us), with the table in LDS before the first reduction.
+    constexpr bool XFIRST = !MX;
+    if (!XFIRST) {
 #pragma unroll
-    for (int k = 0; k < kFirst; ++k) {
-        const int idx = tid + k * NT;  // over the 2 * n4 table vectors
-        tv[k] = idx < n4 ? tsrc[idx] : idx < 2 * n4 ? thsrc[idx - n4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = 0; k < kFirst; ++k) {
+            const int idx = tid + k * NT;  // over the 2 * n4 table vectors
+            tv[k] = idx < n4 ? tsrc[idx] : idx < 2 * n4 ? thsrc[idx - n4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
 
     const int64_t lrow = valid ? row : 0;
@@ -332,23 +366,48 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     };
     load_streamed(kWithX);
 
-#pragma unroll
-    for (int k = 0; k < kFirst; ++k) {
-        const int idx = tid + k * NT;
-        if (idx < 2 * n4)
-            tab[idx] = tv[k];
-    }
-    for (int idx = tid + kFirst * NT; idx < 2 * n4; idx += NT)
-        tab[idx] = idx < n4 ? tsrc[idx] : thsrc[idx - n4];
-
     // Row statistics over the row's WAVES waves (the barriers also publish
     // the LDS table).
     const bool tail_ok = FULL || (VPT - 1) * T + t < nvec;
     auto reduce = [&](float v, int k) { return subgroup_sum(v, red[k], rr * WAVES, WAVES); };
     float d[VPT][8];
-    const float mean = row_mean<VPT>(xv, a.inv_dim, reduce);
-    load_streamed(kAfterMean);
-    const float rstd = row_rstd<VPT>(xv, tail_ok, mean, a.inv_dim, a.eps, reduce, d);
+    float mean, rstd;
+    if (XFIRST) {
+        const float s = thread_sum<VPT>(xv);
+        // The table loads after x has landed (the sum needs it): without
+        // the pin the scheduler hoists them back above the sum.
+        asm volatile("" ::"v"(s));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kFirst; ++k) {
+            const int idx = tid + k * NT;  // over the 2 * n4 table vectors
+            tv[k] = idx < n4 ? tsrc[idx] : idx < 2 * n4 ? thsrc[idx - n4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        mean = reduce(s, 0) * a.inv_dim;
+        load_streamed(kAfterMean);
+        const float q = thread_sumsq<VPT>(xv, tail_ok, mean, d);
+#pragma unroll
+        for (int k = 0; k < kFirst; ++k) {
+            const int idx = tid + k * NT;
+            if (idx < 2 * n4)
+                tab[idx] = tv[k];
+        }
+        for (int idx = tid + kFirst * NT; idx < 2 * n4; idx += NT)
+            tab[idx] = idx < n4 ? tsrc[idx] : thsrc[idx - n4];
+        rstd = rsqrt_refined(reduce(q, 1) * a.inv_dim + a.eps);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kFirst; ++k) {
+            const int idx = tid + k * NT;
+            if (idx < 2 * n4)
+                tab[idx] = tv[k];
+        }
+        for (int idx = tid + kFirst * NT; idx < 2 * n4; idx += NT)
+            tab[idx] = idx < n4 ? tsrc[idx] : thsrc[idx - n4];
+        mean = row_mean<VPT>(xv, a.inv_dim, reduce);
+        load_streamed(kAfterMean);
+        rstd = row_rstd<VPT>(xv, tail_ok, mean, a.inv_dim, a.eps, reduce, d);
+    }
     load_streamed(kAfterRstd);
     if (!valid)
         return;

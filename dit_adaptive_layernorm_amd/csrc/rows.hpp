@@ -52,21 +52,22 @@ __device__ __forceinline__ uint4 ld_row(const uint16_t* row, int i, int nvec, bo
 // caller's pass over the row.  `reduce` sums a value over the row's waves
 // and takes the slot index (0 or 1) of its LDS partials.  row_mean and
 // row_rstd are the two passes on their own, for callers that issue loads
-// between them; row_stats runs both.
-template <int VPT, typename Reduce>
-__device__ __forceinline__ float row_mean(const uint4 (&xv)[VPT], float inv_dim, Reduce reduce)
+// between them; row_stats runs both.  thread_sum and thread_sumsq are a
+// thread's share of each pass before the reduction, for callers that also
+// work between a share and its reduction.
+template <int VPT>
+__device__ __forceinline__ float thread_sum(const uint4 (&xv)[VPT])
 {
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         s = sum_bf16x8(xv[v], s);
-    return reduce(s, 0) * inv_dim;
+    return s;
 }
 
-template <int VPT, typename Reduce>
-__device__ __forceinline__ float row_rstd(const uint4 (&xv)[VPT], bool tail_ok, float mean,
-                                          float inv_dim, float eps, Reduce reduce,
-                                          float (&d)[VPT][8])
+template <int VPT>
+__device__ __forceinline__ float thread_sumsq(const uint4 (&xv)[VPT], bool tail_ok, float mean,
+                                              float (&d)[VPT][8])
 {
     float q = 0.f;
 #pragma unroll
@@ -82,7 +83,21 @@ __device__ __forceinline__ float row_rstd(const uint4 (&xv)[VPT], bool tail_ok, 
                 q = __builtin_fmaf(d[v][e], d[v][e], q);
         }
     }
-    const float var = reduce(q, 1) * inv_dim;
+    return q;
+}
+
+template <int VPT, typename Reduce>
+__device__ __forceinline__ float row_mean(const uint4 (&xv)[VPT], float inv_dim, Reduce reduce)
+{
+    return reduce(thread_sum<VPT>(xv), 0) * inv_dim;
+}
+
+template <int VPT, typename Reduce>
+__device__ __forceinline__ float row_rstd(const uint4 (&xv)[VPT], bool tail_ok, float mean,
+                                          float inv_dim, float eps, Reduce reduce,
+                                          float (&d)[VPT][8])
+{
+    const float var = reduce(thread_sumsq<VPT>(xv, tail_ok, mean, d), 1) * inv_dim;
     return rsqrt_refined(var + eps);
 }
 
