@@ -79,6 +79,10 @@ def parse():
     p.add_argument("--floor-sweep", action="store_true",
                    help="only time the per-token producer and memory-only access patterns over "
                         "a range of row counts at dim 3072 and exit")
+    p.add_argument("--timeline", action="store_true",
+                   help="only record per-wave timelines of the FP8 row and table kernels "
+                        "(libalnp_timeline.so, measurement only) for the FP8 workloads in "
+                        "--only, cold, and exit")
     return p.parse_args()
 
 
@@ -166,6 +170,21 @@ def floor_lib():
 
 # out_kind of alnp_floor_rows
 FLOOR_FP8, FLOOR_NVFP4, FLOOR_BF16, FLOOR_MXFP8, FLOOR_MXFP4, FLOOR_NVFP4_TILED = 0, 1, 2, 3, 4, 5
+
+
+def timeline_lib(alnp):
+    """libalnp_timeline.so: the C ABI with the FP8 row and table kernels
+    writing per-wave clock records (csrc/timeline.hpp), or None."""
+    path = os.path.join(ROOT, "dit_adaptive_layernorm_amd", "libalnp_timeline.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    for fn, (args, res) in alnp.SIGNATURES.items():
+        f = getattr(L, fn)
+        f.argtypes, f.restype = args, res
+    L.alnp_timeline_set.argtypes = [ctypes.c_void_p]
+    L.alnp_timeline_set.restype = ctypes.c_int
+    return L
 
 
 class Producer:
@@ -1031,6 +1050,86 @@ def floor_sweep(torch, alnp, inputs, F, stream, steps, warmup, use_graph, repeat
     print(json.dumps({"floor_sweep": out, "steps": steps, "repeats": repeats}), flush=True)
 
 
+TIMELINE_WORKLOADS = ("ptok_fp8_2520x3072", "table_fp8_2520x3072", "ln_fp8_2520x3072",
+                      "modfp8_fp8_2520x3072", "awq_fp8_2520x3072")
+TIMELINE_REPEATS = 5
+
+
+def timeline_summary(rec, rows):
+    """Summary of one launch's per-wave records (rows x waves, 8 words each;
+    timeline.hpp): phase times in us from the first wave's start, as
+    percentiles (0, 10, 50, 90, 99, 100) over waves, and the median time x
+    landed by a row's dispatch order on its CU."""
+    waves = int(np.count_nonzero(rec[:, 0])) // rows
+    r = rec[: rows * waves].astype(np.float64)
+    if waves == 0 or np.count_nonzero(r[:, 0]) != rows * waves:
+        return {"error": "incomplete records", "waves_per_row": waves}
+    t0 = r[:, 0].min()
+    u = (r[:, :6] - t0) / 100.0                      # 100 MHz clock -> us
+    pct = lambda v: [round(float(np.percentile(v, q)), 2) for q in (0, 10, 50, 90, 99, 100)]
+    out = {"waves_per_row": waves, "end_us": round(float(u[:, 5].max()), 2),
+           "start": pct(u[:, 0]), "x_issued_after_start": pct(u[:, 1] - u[:, 0]),
+           "x_landed": pct(u[:, 2]), "rstd_after_x": pct(u[:, 3] - u[:, 2]),
+           "output_pass": pct(u[:, 4] - u[:, 3]), "stores_done": pct(u[:, 5])}
+    # Rows on each CU (XCC, SE, SH, CU from the XCC_ID and HW_ID registers),
+    # in the order their first wave started.
+    hw = rec[: rows * waves, 7].astype(np.int64).reshape(rows, waves)[:, 0]
+    xcc = rec[: rows * waves, 6].astype(np.int64).reshape(rows, waves)[:, 0] & 0xF
+    cu = (xcc << 8) | (((hw >> 13) & 7) << 5) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 0xF)
+    start = u[:, 0].reshape(rows, waves).min(1)
+    landed = u[:, 2].reshape(rows, waves).max(1)
+    order = np.zeros(rows, np.int64)
+    for c in np.unique(cu):
+        idx = np.nonzero(cu == c)[0]
+        order[idx[np.argsort(start[idx], kind="stable")]] = np.arange(idx.size)
+    out["cus"] = int(np.unique(cu).size)
+    out["x_landed_by_order_on_cu"] = [round(float(np.median(landed[order == k])), 2)
+                                      for k in range(int(order.max()) + 1)]
+    return out
+
+
+def timeline(torch, alnp, inputs, stream, names):
+    """Per-wave timelines: for each workload, TIMELINE_REPEATS launches, each
+    the last of a back-to-back run over the cold rotation of buffer sets, on
+    the timeline build of the library.  Prints one JSON line."""
+    L = timeline_lib(alnp)
+    if L is None:
+        print(json.dumps({"error": "--timeline needs libalnp_timeline.so"}))
+        sys.exit(2)
+    res = {}
+    for name in names:
+        if name not in TIMELINE_WORKLOADS:
+            print(json.dumps({"error": f"--timeline covers {', '.join(TIMELINE_WORKLOADS)}"}))
+            sys.exit(2)
+        d = inputs.make("ln", rows=2520, dim=3072) if name.startswith("ln_") else inputs.workload(name)
+        rows = d["x"].shape[0]
+        sets = sets_for(algorithmic_bytes(name, d), True)
+        prod = Producer(name, d, sets, torch, alnp)
+        calls = [(getattr(L, fn.__name__), args) for fn, args in prod.calls]
+        buf = torch.zeros(rows * 8 * 8, dtype=torch.int64, device="cuda")
+        if L.alnp_timeline_set(buf.data_ptr()) != 0:
+            raise RuntimeError("alnp_timeline_set failed")
+        reps = []
+        for rep in range(TIMELINE_REPEATS):
+            buf.zero_()
+            with torch.cuda.stream(stream):
+                for i in range(sets):
+                    fn, args = calls[(rep + 1 + i) % sets]
+                    st = fn(*args, stream.cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"{name}: status {st}")
+            torch.cuda.synchronize()
+            reps.append(timeline_summary(buf.cpu().numpy().reshape(rows * 8, 8), rows))
+            print(f"# timeline {name} launch {rep}: end {reps[-1].get('end_us')} us",
+                  file=sys.stderr, flush=True)
+        L.alnp_timeline_set(None)
+        torch.cuda.synchronize()
+        res[name] = reps
+        del prod, buf
+        torch.cuda.empty_cache()
+    print(json.dumps({"timeline": res, "clock": "s_memrealtime, 100 MHz", "launches": TIMELINE_REPEATS}))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -1057,6 +1156,10 @@ def main():
         calibrate_copy(torch, floor_lib())
         return
     stream = torch.cuda.Stream()
+    if a.timeline:
+        timeline(torch, alnp, inputs, stream,
+                 [n for n in a.only.split(",") if n] or list(TIMELINE_WORKLOADS))
+        return
     if a.floor_sweep:
         if F is None:
             print(json.dumps({"error": "--floor-sweep needs libalnp_floor.so"}))

@@ -1,8 +1,10 @@
 """Build libalnp.so (the HIP producers and their C ABI) for gfx950 in-tree,
 libalnp_floor.so (memory-only counterparts of the producers, which the
 benchmark times beside them; linked against libalnp.so for its row shapes),
-and the compiled binding _torch_binding (the package's functions in C++ over
-the C ABI: host code only, built with the C++ compiler against torch).
+libalnp_timeline.so (measurement only: the same library with the FP8 row and
+table kernels writing per-wave clock records, csrc/timeline.hpp), and the
+compiled binding _torch_binding (the package's functions in C++ over the C
+ABI: host code only, built with the C++ compiler against torch).
 
     python -m dit_adaptive_layernorm_amd.build      # or build() from Python
 
@@ -24,6 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libalnp.so")
 FLOOR_LIB = os.path.join(PKG, "libalnp_floor.so")
+TIMELINE_LIB = os.path.join(PKG, "libalnp_timeline.so")
 SOURCES = ["producers.hip", "fp4.hip", "rmsmod.hip", "modulation6.hip", "residual.hip", "abi.hip"]
 FLOOR_SOURCE = "floor.hip"
 BINDING_SOURCE = "torch_binding.cpp"
@@ -90,6 +93,12 @@ def build(verbose: bool = False, jobs: int = 7) -> str:
             if src != FLOOR_SOURCE:
                 objs.append(obj)
             procs.append((src, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        # The timeline build's producers next to the product's, both the
+        # longest compiles, so that they start together.
+        tl_obj = os.path.join(tmp, "producers_timeline.o")
+        procs.insert(1, ("producers.hip (timeline)",
+                         [HIPCC, *FLAGS, "-DALNP_TIMELINE", "-c", os.path.join(CSRC, "producers.hip"),
+                          "-o", tl_obj]))
         binding_so = binding_path()
         bind_compile, bind_link = _binding_commands(os.path.join(tmp, "torch_binding.o"),
                                                     binding_so + ".tmp")
@@ -106,6 +115,10 @@ def build(verbose: bool = False, jobs: int = 7) -> str:
               os.path.join(tmp, FLOOR_SOURCE.replace(".hip", ".o")), f"-L{PKG}", "-lalnp",
               "-Wl,-rpath,$ORIGIN", "-o", tmp_floor], verbose)
         os.replace(tmp_floor, FLOOR_LIB)
+        tmp_tl = TIMELINE_LIB + ".tmp"
+        tl_objs = [tl_obj if o.endswith(os.sep + "producers.o") else o for o in objs]
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *tl_objs, "-o", tmp_tl], verbose)
+        os.replace(tmp_tl, TIMELINE_LIB)
         _run(bind_link, verbose)
         os.replace(binding_so + ".tmp", binding_so)
     return LIB

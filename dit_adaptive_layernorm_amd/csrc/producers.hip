@@ -16,6 +16,7 @@
 // FP4 producers live in fp4.hip, the RMSNorm producer in rmsmod.hip, the
 // shared row machinery in rows.hpp.
 #include "rows.hpp"
+#include "timeline.hpp"
 
 // Where a row kernel issues the loads of its streamed operands (per-token
 // scale / shift rows, temb chunks), relative to the row statistics.
@@ -32,7 +33,8 @@ namespace alnp {
 // vector slot (dim / 8 == VPT * WAVES * 64, as for dim 2048 and 3072), so the
 // last slot needs no bounds check, zero fill or predicated stores; the
 // launcher picks it, and the arithmetic is the same.
-template <int VPT, int WAVES, int FORM, bool MX = false, bool FULL = false, bool PRE = false>
+template <int VPT, int WAVES, int FORM, bool MX = false, bool FULL = false, bool PRE = false,
+          bool PAIRS = false>
 __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
 {
     __shared__ float red[32];  // two sets of per-wave partials
@@ -59,6 +61,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
     const int64_t row = grid_row();
     if (row >= a.rows)
         return;  // whole workgroup
+    ALNP_TL_VARS;
+    ALNP_TL_MARK(0);
     {
         // Modulation operands shared by every row ((dim,) vectors, kept in
         // cache) are requested before x.  With kPre the broadcast, modfp8
@@ -90,16 +94,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                     isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, !FULL && v == VPT - 1);
             }
         } else if (FORM == kModFp8) {
+            // PAIRS (kPre FP8 rows that fill every slot, operands 16-byte
+            // aligned; the launcher checks): lane pairs halve the load
+            // instructions issued ahead of x.  The even lane loads 16 scale
+            // bytes and the odd lane 16 shift bytes for the pair's two
+            // vectors (8 * (i & ~1), inside the row since the slot count is
+            // even), and each passes the other the half it needs.  2520 x
+            // 3072 cold 6.76 -> 6.67 us (A-B, bit-identical); as a run-time
+            // branch in one kernel 6.95, and in the FP4 kernel slower.
+            constexpr bool kPairs = PAIRS && kPre && FULL && !MX;
+            if (kPairs) {
+                const bool odd = t & 1;
+                const uint8_t* src = odd ? a.shift_fp8 : a.scale_fp8;
 #pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
-                sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
+                for (int v = 0; v < VPT; ++v) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * ((v * T + t) & ~1));
+                    const uint32_t s0 = odd ? w.x : w.z, s1 = odd ? w.y : w.w;
+                    const uint32_t r0 = __builtin_amdgcn_mov_dpp(s0, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+                    const uint32_t r1 = __builtin_amdgcn_mov_dpp(s1, 0xB1, 0xF, 0xF, false);
+                    sc8[v] = odd ? make_uint2(r0, r1) : make_uint2(w.x, w.y);
+                    sh8[v] = odd ? make_uint2(w.z, w.w) : make_uint2(r0, r1);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    sc8[v] = ld_fp8x8(a.scale_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
+                    sh8[v] = ld_fp8x8(a.shift_fp8, v * T + t, nvec, !FULL && v == VPT - 1);
+                }
             }
         }
         uint4 xv[VPT];
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
             xv[v] = ld_row<true>(a.x + row * dim, v * T + t, nvec, !FULL && v == VPT - 1);
+        ALNP_TL_MARK(1);
         const float sdeq = FORM == kModFp8 ? *a.scale_deq : 0.f;
         const float hdeq = FORM == kModFp8 ? *a.shift_deq : 0.f;
         // tp = 1 + scale, hp = shift (fp32, the same roundings as in the
@@ -181,7 +209,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
         const bool tail_ok = FULL || (VPT - 1) * T + t < nvec;
         auto reduce = [&](float v, int k) { return group_sum(v, red + 16 * k, WAVES); };
         float d[VPT][8];
-        const float mean = row_mean<VPT>(xv, a.inv_dim, reduce);
+        const float xsum = thread_sum<VPT>(xv);
+        ALNP_TL_MARK_AFTER(2, xsum);
+        const float mean = reduce(xsum, 0) * a.inv_dim;
         load_streamed(kAfterMean);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
@@ -191,6 +221,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
                 isv[v] = ld_row<false>(a.inv_s, v * T + t, nvec, !FULL && v == VPT - 1);
         }
         const float rstd = row_rstd<VPT>(xv, tail_ok, mean, a.inv_dim, a.eps, reduce, d);
+        ALNP_TL_MARK_AFTER(3, rstd);
         load_streamed(kAfterRstd);
 
 #pragma unroll
@@ -276,6 +307,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_adaln_fp8_rows(Fp8Args a)
             if (a.row_mean) a.row_mean[row] = mean;
             if (a.row_rstd) a.row_rstd[row] = rstd;
         }
+        ALNP_TL_MARK(4);
+        ALNP_TL_RECORD(row, WAVES);
     }
 }
 
@@ -314,6 +347,8 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     const float inv = MX ? 0.f : 1.0f / *a.act_scale;
     const int64_t row = grid_row() * R + rr;
     const bool valid = row < a.rows;
+    ALNP_TL_VARS;
+    ALNP_TL_MARK(0);
 
     // The table rows: up to 8 float4 per thread in flight, the rest (only for
     // dims above 4 * 2 * NT ... 8192) loaded while they are written to LDS.
@@ -350,6 +385,7 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         xv[v] = ld_row<true>(xr, v * T + t, nvec, !FULL && v == VPT - 1);
+    ALNP_TL_MARK(1);
     // The temb chunks are requested after the first reduction (FP8) or the
     // second (MXFP8), as in k_adaln_fp8_rows; those points measured best
     // for this kernel (2520 x 3072 cold: FP8 11.33 -> 10.95 us, MXFP8 11.42
@@ -374,6 +410,7 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
     float mean, rstd;
     if (XFIRST) {
         const float s = thread_sum<VPT>(xv);
+        ALNP_TL_MARK_AFTER(2, s);
         // The table loads after x has landed (the sum needs it): without
         // the pin the scheduler hoists them back above the sum.
         asm volatile("" ::"v"(s));
@@ -404,10 +441,13 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
         }
         for (int idx = tid + kFirst * NT; idx < 2 * n4; idx += NT)
             tab[idx] = idx < n4 ? tsrc[idx] : thsrc[idx - n4];
-        mean = row_mean<VPT>(xv, a.inv_dim, reduce);
+        const float s = thread_sum<VPT>(xv);
+        ALNP_TL_MARK_AFTER(2, s);
+        mean = reduce(s, 0) * a.inv_dim;
         load_streamed(kAfterMean);
         rstd = row_rstd<VPT>(xv, tail_ok, mean, a.inv_dim, a.eps, reduce, d);
     }
+    ALNP_TL_MARK_AFTER(3, rstd);
     load_streamed(kAfterRstd);
     if (!valid)
         return;
@@ -451,6 +491,8 @@ __global__ __launch_bounds__(R * WAVES * 64) void k_adaln_fp8_table_lds(Fp8Args 
         if (a.row_mean) a.row_mean[row] = mean;
         if (a.row_rstd) a.row_rstd[row] = rstd;
     }
+    ALNP_TL_MARK(4);
+    ALNP_TL_RECORD(row, WAVES);
 }
 
 __global__ __launch_bounds__(256) void k_adaln_fp8_block(Fp8Args a, int form)
@@ -594,13 +636,14 @@ RowShape row_shape(int dim)
 // Both orders compute the same bits.
 constexpr int64_t kPreMinRows = 512;
 
-template <int FORM, bool MX, bool PRE>
+template <int FORM, bool MX, bool PRE, bool PAIRS = false>
 static hipError_t launch_fp8_rows_as(const Fp8Args& a, RowShape rs, hipStream_t s)
 {
     const dim3 grid = row_grid(a.rows);
     if ((a.dim >> 3) == rs.vpt * rs.threads) {
-#define ALNP_LAUNCH(V, W) \
-    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, MX, true, PRE && V <= 3>), grid, dim3(W * 64), 0, s, a)
+#define ALNP_LAUNCH(V, W)                                                                           \
+    hipLaunchKernelGGL((k_adaln_fp8_rows<V, W, FORM, MX, true, PRE && V <= 3, PAIRS && PRE && V <= 3>), \
+                       grid, dim3(W * 64), 0, s, a)
         ALNP_SHAPE_CASES(ALNP_LAUNCH)
 #undef ALNP_LAUNCH
         return hipGetLastError();
@@ -616,8 +659,13 @@ template <int FORM, bool MX = false>
 static hipError_t launch_fp8_rows(const Fp8Args& a, RowShape rs, hipStream_t s)
 {
     constexpr bool kShared = FORM == kBcast || FORM == kModFp8 || FORM == kAwq;
-    if (kShared && a.rows >= kPreMinRows)
+    if (kShared && a.rows >= kPreMinRows) {
+        constexpr bool kPairs = FORM == kModFp8 && !MX;
+        if (kPairs && ((reinterpret_cast<uintptr_t>(a.scale_fp8) |
+                        reinterpret_cast<uintptr_t>(a.shift_fp8)) & 15) == 0)
+            return launch_fp8_rows_as<FORM, MX, kShared, kPairs>(a, rs, s);
         return launch_fp8_rows_as<FORM, MX, kShared>(a, rs, s);
+    }
     return launch_fp8_rows_as<FORM, MX, false>(a, rs, s);
 }
 
@@ -729,3 +777,14 @@ hipError_t launch_quant_fp8(const float* v, const float* act, int64_t n, uint8_t
 }
 
 }  // namespace alnp
+
+#ifdef ALNP_TIMELINE
+// Measurement-only build: the buffer the FP8 row and table kernels write
+// their per-wave records to (timeline.hpp).  Not part of the product ABI.
+__device__ unsigned long long* alnp::timeline_buf;
+
+extern "C" int alnp_timeline_set(void* buf)
+{
+    return hipMemcpyToSymbol(HIP_SYMBOL(alnp::timeline_buf), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
+}
+#endif

@@ -342,6 +342,36 @@ def _shared_operand_call(kind, mx, x, d):
     return host_u8(o), None, mean.cpu().numpy(), rstd.cpu().numpy()
 
 
+@pytest.mark.parametrize("dim", [2048, 3072])
+def test_modfp8_operands_on_8_byte_boundaries(orc, dim):
+    """Rows that fill every slot, from 512 rows: the FP8 modfp8 form loads its
+    e4m3 operands in lane pairs (16 bytes per lane) when both are 16-byte
+    aligned, and eight bytes per lane otherwise.  Operands that start 8 bytes
+    past a 16-byte boundary give the same codes and row statistics as
+    aligned ones."""
+    print(f"modfp8 operand alignment dim={dim}", flush=True)
+    rows = 1030
+    d = modfp8_inputs(rows, dim, seed=43)
+    x = dev_bf16(d["x"])
+    outs = []
+    for off in (0, 8):
+        s8 = torch.zeros(dim + 16, dtype=torch.uint8, device="cuda")
+        h8 = torch.zeros(dim + 16, dtype=torch.uint8, device="cuda")
+        s8[off:off + dim] = torch.from_numpy(d["scale_fp8"]).cuda()
+        h8[off:off + dim] = torch.from_numpy(d["shift_fp8"]).cuda()
+        sv, hv = s8[off:off + dim].view(torch.float8_e4m3fn), h8[off:off + dim].view(torch.float8_e4m3fn)
+        assert (sv.data_ptr() % 16 == 0) == (off == 0)
+        mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+        rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+        o = alnp.ada_layer_norm_quant_fp8_modfp8_bf16(x, sv, hv, scalar(0.75), scalar(1.5), act(),
+                                                     row_mean=mean, row_rstd=rstd)
+        outs.append((host_u8(o), mean.cpu().numpy(), rstd.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ref = orc.adaln_fp8_modfp8(d["x"], d["scale_fp8"], d["shift_fp8"], 0.75, 1.5, 0.025)[0]
+    assert_codes_close(outs[0][0], ref, e4m3_ordinal, f"modfp8 lane pairs {rows}x{dim}")
+
+
 @pytest.mark.parametrize("mx", [False, True])
 @pytest.mark.parametrize("kind", ["bcast", "modfp8", "awq"])
 def test_shared_operand_forms_same_bytes_across_the_row_threshold(kind, mx):
