@@ -138,41 +138,61 @@ struct FloorMod6Args {
     uint16_t* out[6];
 };
 
-// The six-way producer's mapping (thread = one 8-element slot of the six
-// chunks x 4 tokens, every load issued before the first store); the output is
-// the upper half of each fp32 (truncation) instead of the rounded sum.
+// The six-way producer's mapping (a wave per 512 consecutive floats of a
+// token's span, two contiguous 1 KiB loads per token, 4 tokens, every load
+// issued before the first store, lane pairs storing 16 bytes each after one
+// DPP swap); the output is the upper half of each fp32 (truncation) instead
+// of the rounded sum.
 __global__ __launch_bounds__(256) void k_floor_mod6(FloorMod6Args a)
 {
-    const int dv = a.dim >> 3;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= 6 * dv)
-        return;
-    const int k = (i >= dv) + (i >= 2 * dv) + (i >= 3 * dv) + (i >= 4 * dv) + (i >= 5 * dv);
-    const int j8 = i - k * dv;
-    uint16_t* out = a.out[0];
+    const int span = 6 * a.dim;
+    const int blk = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;
+    if (blk >= span)
+        return;  // whole wave
+    const int lane = threadIdx.x & 63;
+    int e[2], k[2];
+    bool ok[2];
 #pragma unroll
-    for (int c = 1; c < 6; ++c)
-        out = k == c ? a.out[c] : out;
+    for (int h = 0; h < 2; ++h) {
+        const int eh = blk + 256 * h + 4 * lane;
+        ok[h] = eh < span;
+        e[h] = ok[h] ? eh : 0;
+        k[h] = (e[h] >= a.dim) + (e[h] >= 2 * a.dim) + (e[h] >= 3 * a.dim) + (e[h] >= 4 * a.dim) +
+               (e[h] >= 5 * a.dim);
+    }
     const int64_t t0 = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * kTokensPerThread;
-    uint4 p0[kTokensPerThread], p1[kTokensPerThread];
+    uint4 p[kTokensPerThread][2];
 #pragma unroll
     for (int u = 0; u < kTokensPerThread; ++u) {
         const int64_t t = t0 + u < a.tokens ? t0 + u : a.tokens - 1;
-        const float* pt = a.params + t * 6 * (int64_t)a.dim + 8 * (int64_t)i;
-        p0[u] = ld_stream(pt);
-        p1[u] = ld_stream(pt + 4);
+        const float* pt = a.params + t * span;
+        p[u][0] = ld_stream(pt + e[0]);
+        p[u][1] = ld_stream(pt + e[1]);
     }
+    const bool odd = lane & 1;
+    const int hs = odd ? 1 : 0;
+    uint16_t* out = a.out[0];
+#pragma unroll
+    for (int c = 1; c < 6; ++c)
+        out = k[hs] == c ? a.out[c] : out;
+    const int js = (odd ? e[1] - 4 : e[0]) - k[hs] * a.dim;
 #pragma unroll
     for (int u = 0; u < kTokensPerThread; ++u) {
         const int64_t t = t0 + u;
         if (t >= a.tokens)
             break;
-        uint4 o;
-        o.x = (p0[u].x >> 16) | (p0[u].y & 0xFFFF0000u);
-        o.y = (p0[u].z >> 16) | (p0[u].w & 0xFFFF0000u);
-        o.z = (p1[u].x >> 16) | (p1[u].y & 0xFFFF0000u);
-        o.w = (p1[u].z >> 16) | (p1[u].w & 0xFFFF0000u);
-        st_stream(out + t * a.dim + 8 * (int64_t)j8, o);
+        uint2 o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            o[h].x = (p[u][h].x >> 16) | (p[u][h].y & 0xFFFF0000u);
+            o[h].y = (p[u][h].z >> 16) | (p[u][h].w & 0xFFFF0000u);
+        }
+        const uint2 snd = odd ? o[0] : o[1];
+        const uint32_t r0 = __builtin_amdgcn_mov_dpp(snd.x, 0xB1, 0xF, 0xF, false);
+        const uint32_t r1 = __builtin_amdgcn_mov_dpp(snd.y, 0xB1, 0xF, 0xF, false);
+        if (ok[hs])
+            st_stream(out + t * a.dim + js, odd ? make_uint4(r0, r1, o[1].x, o[1].y)
+                                                : make_uint4(o[0].x, o[0].y, r0, r1));
     }
 }
 
@@ -303,10 +323,10 @@ extern "C" int alnp_floor_modulation6(const float* params, int64_t tokens, int d
             return -1;
         a.out[k] = out[k];
     }
-    const int64_t slots = 6 * (int64_t)(dim >> 3);
+    const int64_t waves = (6 * (int64_t)dim + 511) / 512;
     const int64_t groups = (tokens + kTokensPerThread - 1) / kTokensPerThread;
     const int64_t gy = groups < 65535 ? groups : 65535;
-    const dim3 grid((unsigned)((slots + 255) / 256), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
+    const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
     hipLaunchKernelGGL(k_floor_mod6, grid, dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }

@@ -5,14 +5,19 @@
 // shape (batch, seq, 6, dim) and an fp32 (6, dim) per-layer table in, six
 // bf16 (batch, seq, dim) tensors out).
 //
-// A pure stream: 4 bytes read and 2 written per element, one add.  Each
-// thread owns one 8-element slot of the (6, dim) span and handles it for four
-// consecutive tokens: the matching slot of the (6, dim) table is loaded once
-// into registers, the eight 16-byte non-temporal params loads are all in
-// flight before the first 16-byte non-temporal store.  Consecutive threads
-// take consecutive slots, so every wave access is 1 KiB contiguous.  (Reading
-// the table per token instead cost 7% extra HBM fetches, as streamed params
-// evicted it from L2, and ~20% in time.)
+// A pure stream: 4 bytes read and 2 written per element, one add.  Each wave
+// owns 512 consecutive floats of a token's (6, dim) span and handles them for
+// four consecutive tokens: its lanes read them as two contiguous 1 KiB loads
+// per token (lane j: floats 4j..4j+3 of each 256-float half), the matching
+// table values are loaded once into registers, and all eight 16-byte
+// non-temporal params loads are in flight before the first store.  A lane pair
+// then holds eight consecutive outputs per half; one DPP swap lets the even
+// lane store half 0 and the odd lane half 1, 16 bytes each, non-temporal.
+// (Reading the table per token instead cost 7% extra HBM fetches, as
+// streamed params evicted it from L2, and ~20% in time.  The earlier mapping,
+// a lane per 8-float slot, read 32 bytes per lane as two loads that each
+// touched every line of a 2 KiB span half: 97.2 us against 90.0 on the
+// 1 x 5070 x 3072 workload, A-B, bit-identical.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -35,46 +40,64 @@ __device__ __forceinline__ float4 as_f4(const uint4& u)
                        __uint_as_float(u.w));
 }
 
-// Tokens per thread in the vector kernel.
+// Tokens per thread in the vector kernel (2 and 8 measured slower).
 constexpr int kTokensPerThread = 4;
 
-// A thread owns one 8-element slot i of the token span (chunk k, columns
-// 8*j8 .. 8*j8+7) and walks kTokensPerThread consecutive tokens: the table
-// slot is read once into registers and reused, and all of the thread's
-// params loads are in flight before the first store.  blockIdx.x picks 256
-// slots, (blockIdx.y, blockIdx.z) the token group.
+// Wave w of workgroup blockIdx.x covers floats [512 (4 blockIdx.x + w), + 512)
+// of the span (6 * dim floats per token, dim % 8 == 0, so a lane pair's eight
+// floats lie in one chunk and wholly inside or outside the span); lanes past
+// the span load a valid address and store nothing.  (blockIdx.y, blockIdx.z)
+// pick the token group.
 __global__ __launch_bounds__(256) void k_mod6_vec(Mod6Args a)
 {
-    const int dv = a.dim >> 3;  // 8-element vectors per chunk
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= 6 * dv)
-        return;
-    const int k = (i >= dv) + (i >= 2 * dv) + (i >= 3 * dv) + (i >= 4 * dv) + (i >= 5 * dv);
-    const int j8 = i - k * dv;
-    uint16_t* out = select_out(a, k);
-    const float4* mk = reinterpret_cast<const float4*>(a.mod + (int64_t)k * a.dim) + 2 * j8;
-    const float4 m0 = mk[0], m1 = mk[1];
+    const int span = 6 * a.dim;
+    const int blk = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;
+    if (blk >= span)
+        return;  // whole wave
+    const int lane = threadIdx.x & (kWave - 1);
+    int e[2], k[2];
+    bool ok[2];
+    float4 m[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int eh = blk + 256 * h + 4 * lane;
+        ok[h] = eh < span;
+        e[h] = ok[h] ? eh : 0;
+        k[h] = (e[h] >= a.dim) + (e[h] >= 2 * a.dim) + (e[h] >= 3 * a.dim) + (e[h] >= 4 * a.dim) +
+               (e[h] >= 5 * a.dim);
+        m[h] = *reinterpret_cast<const float4*>(a.mod + e[h]);
+    }
     const int64_t t0 = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * kTokensPerThread;
-    uint4 p0[kTokensPerThread], p1[kTokensPerThread];
+    uint4 p[kTokensPerThread][2];
 #pragma unroll
     for (int u = 0; u < kTokensPerThread; ++u) {
         const int64_t t = t0 + u < a.tokens ? t0 + u : a.tokens - 1;
-        const float* pt = a.params + t * 6 * (int64_t)a.dim + 8 * (int64_t)i;
-        p0[u] = ld_stream(pt);
-        p1[u] = ld_stream(pt + 4);
+        const float* pt = a.params + t * span;
+        p[u][0] = ld_stream(pt + e[0]);
+        p[u][1] = ld_stream(pt + e[1]);
     }
+    const bool odd = lane & 1;
+    const int hs = odd ? 1 : 0;                        // the half this lane stores
+    uint16_t* out = select_out(a, k[hs]);
+    const int js = (odd ? e[1] - 4 : e[0]) - k[hs] * a.dim;  // its pair's first element
 #pragma unroll
     for (int u = 0; u < kTokensPerThread; ++u) {
         const int64_t t = t0 + u;
         if (t >= a.tokens)
             break;
-        const float4 q0 = as_f4(p0[u]), q1 = as_f4(p1[u]);
-        uint4 o;
-        o.x = pack_bf16x2(q0.x + m0.x, q0.y + m0.y);
-        o.y = pack_bf16x2(q0.z + m0.z, q0.w + m0.w);
-        o.z = pack_bf16x2(q1.x + m1.x, q1.y + m1.y);
-        o.w = pack_bf16x2(q1.z + m1.z, q1.w + m1.w);
-        st_stream(out + t * a.dim + 8 * (int64_t)j8, o);
+        uint2 o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float4 q = as_f4(p[u][h]);
+            o[h].x = pack_bf16x2(q.x + m[h].x, q.y + m[h].y);
+            o[h].y = pack_bf16x2(q.z + m[h].z, q.w + m[h].w);
+        }
+        const uint2 snd = odd ? o[0] : o[1];
+        const uint32_t r0 = __builtin_amdgcn_mov_dpp(snd.x, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+        const uint32_t r1 = __builtin_amdgcn_mov_dpp(snd.y, 0xB1, 0xF, 0xF, false);
+        if (ok[hs])
+            st_stream(out + t * a.dim + js, odd ? make_uint4(r0, r1, o[1].x, o[1].y)
+                                                : make_uint4(o[0].x, o[0].y, r0, r1));
     }
 }
 
@@ -96,10 +119,10 @@ __global__ __launch_bounds__(256) void k_mod6_scalar(Mod6Args a)
 hipError_t launch_modulation6(const Mod6Args& a, bool fast, hipStream_t s)
 {
     if (fast) {
-        const int64_t slots = 6 * (int64_t)(a.dim >> 3);
+        const int64_t waves = (6 * (int64_t)a.dim + 511) / 512;
         const int64_t groups = (a.tokens + kTokensPerThread - 1) / kTokensPerThread;
         const int64_t gy = groups < 65535 ? groups : 65535;
-        const dim3 grid((unsigned)((slots + 255) / 256), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
+        const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)gy, (unsigned)((groups + gy - 1) / gy));
         hipLaunchKernelGGL(k_mod6_vec, grid, dim3(256), 0, s, a);
     } else {
         const dim3 grid((unsigned)(a.tokens < (1 << 20) ? a.tokens : (1 << 20)));
