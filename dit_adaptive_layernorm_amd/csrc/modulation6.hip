@@ -8,16 +8,16 @@
 // A pure stream: 4 bytes read and 2 written per element, one add.  Each wave
 // owns 512 consecutive floats of a token's (6, dim) span and handles them for
 // four consecutive tokens: its lanes read them as two contiguous 1 KiB loads
-// per token (lane j: floats 4j..4j+3 of each 256-float half), the matching
-// table values are loaded once into registers, and all eight 16-byte
-// non-temporal params loads are in flight before the first store.  A lane pair
-// then holds eight consecutive outputs per half; one DPP swap lets the even
-// lane store half 0 and the odd lane half 1, 16 bytes each, non-temporal.
-// (Reading the table per token instead cost 7% extra HBM fetches, as
-// streamed params evicted it from L2, and ~20% in time.  The earlier mapping,
-// a lane per 8-float slot, read 32 bytes per lane as two loads that each
-// touched every line of a 2 KiB span half: 97.2 us against 90.0 on the
-// 1 x 5070 x 3072 workload, A-B, bit-identical.)
+// per token (lane j: floats 4j..4j+3 of each 256-float half), all eight
+// 16-byte non-temporal params loads are in flight before the first store, and
+// the matching table values are loaded once into registers after them.  A
+// lane pair then holds eight consecutive outputs per half; one DPP swap lets
+// the even lane store half 0 and the odd lane half 1, 16 bytes each,
+// non-temporal.  (Reading the table per token instead cost 7% extra HBM
+// fetches, as streamed params evicted it from L2, and ~20% in time.  The
+// earlier mapping, a lane per 8-float slot, read 32 bytes per lane as two
+// loads that each touched every line of a 2 KiB span half: 97.2 us against
+// 90.0 on the 1 x 5070 x 3072 workload, A-B, bit-identical.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -65,7 +65,6 @@ __global__ __launch_bounds__(256) void k_mod6_vec(Mod6Args a)
         e[h] = ok[h] ? eh : 0;
         k[h] = (e[h] >= a.dim) + (e[h] >= 2 * a.dim) + (e[h] >= 3 * a.dim) + (e[h] >= 4 * a.dim) +
                (e[h] >= 5 * a.dim);
-        m[h] = *reinterpret_cast<const float4*>(a.mod + e[h]);
     }
     const int64_t t0 = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * kTokensPerThread;
     uint4 p[kTokensPerThread][2];
@@ -76,6 +75,13 @@ __global__ __launch_bounds__(256) void k_mod6_vec(Mod6Args a)
         p[u][0] = ld_stream(pt + e[0]);
         p[u][1] = ld_stream(pt + e[1]);
     }
+    // The table values (L2 hits) after the params loads, which they would
+    // otherwise hold up in the CU's load queue (a scheduling barrier keeps
+    // them there): 89.2 -> 88.3 us (A-B, bit-identical).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        m[h] = *reinterpret_cast<const float4*>(a.mod + e[h]);
     const bool odd = lane & 1;
     const int hs = odd ? 1 : 0;                        // the half this lane stores
     uint16_t* out = select_out(a, k[hs]);
