@@ -130,19 +130,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
         xv[0][v] = ld_row<true>(a.x + r0 * dim, v * T + t, nvec, v == VPT - 1);
-    // The second row's x too before the weight and the segment's rows (L2
-    // hits): a CU's loads queue behind each other, and loads issued ahead of
-    // x hold up the x of its later rows.  37810 x 5376: 140.4 -> 138.5 us
-    // (A-B, bit-identical).
+    // The second row's x too, before anything else: a CU's loads queue
+    // behind each other, and loads issued ahead of x hold up the x of its
+    // later rows.  37810 x 5376: 140.4 -> 138.5 us (A-B, bit-identical).
     if (SPAN > 1 && n > 1) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
             xv[1][v] = ld_row<true>(a.x + (r0 + 1) * dim, v * T + t, nvec, v == VPT - 1);
-    }
-    if (W) {
-#pragma unroll
-        for (int v = 0; v < VPT; ++v)
-            wv[v] = ld_row<false>(a.weight, v * T + t, nvec, v == VPT - 1);
     }
     int64_t cur = -1;  // segment whose rows tv / shv hold
 #pragma unroll
@@ -153,23 +147,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
         const int32_t sidx = __builtin_amdgcn_readlane(segv, k);
         const bool in_range = sidx >= 0 && sidx < a.segments;
         const int64_t srow = in_range ? sidx : 0;
-        if (srow != cur) {
-            uint4 scv[VPT];
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                scv[v] = ld_row<false>(a.scale + srow * dim, v * T + t, nvec, v == VPT - 1);
-                shv[v] = ld_row<false>(a.shift + srow * dim, v * T + t, nvec, v == VPT - 1);
-            }
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                float sc[8];
-                unpack8(scv[v], sc);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    tv[v][e] = bf16_round(sc[e] + 1.0f);
-            }
-            cur = srow;
-        }
         const uint4(&x)[VPT] = xv[k & 1];
         if (k + 1 < n && k + 1 >= 2) {
 #pragma unroll
@@ -180,7 +157,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_rms_mod_span(RmsArgs a)
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
             q = sumsq_bf16x8(x[v], q);
+        // The weight and the segment's rows (L2 hits) are requested once
+        // this row's x has landed (its sum of squares is formed), not with
+        // x: loads a CU issues ahead of its later rows' x hold those up in
+        // its load queue, and these arrive while the sum is exchanged.
+        // 37810 x 5376: 138.3 -> 134.3 us (A-B, bit-identical).
+        const bool fresh = srow != cur;
+        uint4 scv[VPT];
+        if (k == 0 || fresh) {
+            asm volatile("" ::"v"(q));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (W && k == 0) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+                wv[v] = ld_row<false>(a.weight, v * T + t, nvec, v == VPT - 1);
+        }
+        if (fresh) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                scv[v] = ld_row<false>(a.scale + srow * dim, v * T + t, nvec, v == VPT - 1);
+                shv[v] = ld_row<false>(a.shift + srow * dim, v * T + t, nvec, v == VPT - 1);
+            }
+        }
         const float rstd = rsqrt_refined(group_sum(q, red[k & 1], WAVES) * a.inv_dim + a.eps);
+        if (fresh) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                float sc[8];
+                unpack8(scv[v], sc);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    tv[v][e] = bf16_round(sc[e] + 1.0f);
+            }
+            cur = srow;
+        }
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int i = v * T + t;
